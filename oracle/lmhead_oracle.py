@@ -1,0 +1,222 @@
+"""CPU oracle for the LM-head logits projection -- TEST INFRASTRUCTURE ONLY.
+
+    logits[m, v] = alpha * (hidden[m, :] . W[v, :]) + bias[v]
+
+This module is the slow, plain definition that the GPU library is checked
+against. It is imported only by the test-suite, by the smoke check and by the
+CPU-baseline leg of the benchmark; the library itself never calls it and
+shares no code with it (its own bf16 / E2M1 / E4M3 decoders and roundings are
+written here from the format definitions).
+
+What the pages fix, and where (page title, then section):
+
+* The projection accumulates bf16 inputs at fp32 precision and never builds an
+  fp32 copy of the weight -- sglang PR 32370 digest ("FP32 LM head skips the
+  FP32 cast"), sections on motivation and implementation breakdown; vLLM PR
+  49120 ("Honor fp32 head_dtype in Inkling muP logits"), section Purpose.
+* The muP divisor enters as alpha = 1/mup, and folding it into the GEMM gives
+  the same bits as the projection followed by a separate elementwise multiply
+  -- vLLM PR 49120, sections Purpose and "muP is folded into the fp32 GEMM".
+  The oracle therefore applies alpha *after* rounding the dot product to fp32,
+  as that separate multiply does.
+* An embedding bias may be added to the logits -- sglang digest, key source
+  excerpt of ``_compute_lm_head`` (the ``embedding_bias`` argument).
+* The NVFP4 head is weight-only 4-bit with 16-bit activations, and a row's
+  logits may not depend on how many rows are in the call -- metrale
+  ``lm_head_nvfp4_rows.rs`` source page, module documentation.
+
+Readings where the pages are silent (each listed in the design notes):
+
+* fp32 output: r = fl32(S); r = fl32(r * alpha); with bias r = fl32(r + b),
+  every step an IEEE binary32 round-to-nearest-even operation, S the dot
+  product accumulated in binary64 (each bf16 x bf16 product is exact there).
+* bf16 output: the binary64 value alpha*S (+ b) correctly rounded to bf16
+  (round-to-odd into binary32, then nearest-even into bf16: S. Boldo and
+  G. Melquiond, "Emulation of FMA and correctly rounded sums: proved
+  algorithms using rounding to odd", IEEE Trans. Computers 57(4), 2008).
+* NVFP4 layout: codes [V, H/2] row-major, element 2i in the low nibble of byte
+  i and 2i+1 in the high nibble; one OCP E4M3 scale per 16 consecutive
+  elements of a weight row, [V, H/16] row-major; one fp32 per-tensor scale g.
+  w = e2m1(code) * e4m3(scale) (exact), and the output is g*alpha*S (+ b)
+  correctly rounded to bf16.
+
+Parity pins (tests marked "not gpu"): a hand-computed 2x3x4 example and a
+hand-computed NVFP4 example (tests/golden), exact rational brute force with
+``fractions.Fraction`` on tiny random cases, exact integer arithmetic checked
+against numpy's int64 matmul, E4M3 decoding checked against torch's
+float8_e4m3fn, bf16 decoding and rounding checked against torch.bfloat16, the
+E2M1 magnitudes of the OCP MX specification, one-hot weights (a gather) and
+zero hidden rows (bias only).
+"""
+from __future__ import annotations
+
+import numpy as np
+
+# ----------------------------------------------------------------------------
+# Number formats, written from their definitions.
+# ----------------------------------------------------------------------------
+
+
+def bf16_to_f64(bits) -> np.ndarray:
+    """bfloat16 is the upper 16 bits of an IEEE binary32; widening is exact."""
+    b = np.asarray(bits, dtype=np.uint16)
+    with np.errstate(invalid="ignore"):          # NaN patterns widen to NaN
+        return (b.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def e2m1_to_f64(code) -> np.ndarray:
+    """OCP MX FP4 E2M1: sign bit 3, exponent bits 2..1 (bias 1), mantissa bit 0.
+
+    Exponent field 0 is subnormal: value = mantissa * 1/2. Otherwise
+    value = 2^(e-1) * (1 + mantissa/2). No infinities or NaNs.
+    """
+    c = np.asarray(code, dtype=np.int64)
+    sign = (c >> 3) & 1
+    e = (c >> 1) & 3
+    m = c & 1
+    mag = np.where(e == 0, m * 0.5, np.ldexp(1.0 + m * 0.5, (e - 1)))
+    return np.where(sign == 1, -mag, mag).astype(np.float64)
+
+
+def e4m3_to_f64(byte) -> np.ndarray:
+    """OCP FP8 E4M3: sign bit 7, exponent bits 6..3 (bias 7), mantissa bits 2..0.
+
+    Exponent field 0 is subnormal: value = 2^-6 * m/8. Exponent 15 with
+    mantissa 7 is NaN (the only NaN pattern); there are no infinities.
+    """
+    b = np.asarray(byte, dtype=np.int64)
+    sign = (b >> 7) & 1
+    e = (b >> 3) & 15
+    m = b & 7
+    mag = np.where(e == 0, np.ldexp(m / 8.0, -6), np.ldexp(1.0 + m / 8.0, e - 7))
+    mag = np.where((e == 15) & (m == 7), np.nan, mag)
+    return np.where(sign == 1, -mag, mag).astype(np.float64)
+
+
+def unpack_e2m1(packed, H: int) -> np.ndarray:
+    """[V, H/2] bytes -> [V, H] codes; element 2i is the low nibble of byte i."""
+    p = np.asarray(packed, dtype=np.uint8)
+    out = np.empty(p.shape[:-1] + (H,), dtype=np.uint8)
+    out[..., 0::2] = p & 0x0F
+    out[..., 1::2] = p >> 4
+    return out
+
+
+def nvfp4_weight_f64(packed, scale_bytes, H: int) -> np.ndarray:
+    """Dequantised NVFP4 weight w[v, k] = e2m1(code[v, k]) * e4m3(scale[v, k // 16]).
+
+    The per-tensor scale g is not folded in here (it is applied to the sum).
+    The product of a 2-bit and a 4-bit significand is exact in binary64.
+    """
+    codes = unpack_e2m1(packed, H)
+    s = e4m3_to_f64(scale_bytes)
+    return e2m1_to_f64(codes) * np.repeat(s, 16, axis=-1)
+
+
+def f32_to_bf16_rne(x) -> np.ndarray:
+    """binary32 -> bf16 bits, round to nearest, ties to even (NaN stays quiet)."""
+    u = np.asarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    is_nan = (u & 0x7FFFFFFF) > 0x7F800000
+    r = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
+    r = np.where(is_nan, (u >> 16) | 0x40, r)
+    return r.astype(np.uint16)
+
+
+def f64_to_f32_round_to_odd(x) -> np.ndarray:
+    """binary64 -> binary32 with rounding to odd: exact values stay, inexact
+    ones take the neighbour whose last significand bit is 1.
+    Finite inputs within binary32 range only."""
+    x = np.asarray(x, dtype=np.float64)
+    f = x.astype(np.float32)                      # nearest-even
+    back = f.astype(np.float64)
+    inexact = back != x
+    # the binary32 neighbour toward zero
+    toward0 = np.where(np.abs(back) > np.abs(x), np.nextafter(f, np.float32(0.0)), f)
+    bits = toward0.view(np.uint32)
+    bits = np.where(inexact, bits | np.uint32(1), bits)
+    return bits.astype(np.uint32).view(np.float32)
+
+
+def f64_to_bf16_correct(x) -> np.ndarray:
+    """binary64 -> bf16 bits, correctly rounded (nearest even) from binary64.
+
+    Round to odd into binary32 (24 >= 8 + 2 bits), then nearest-even into
+    bf16; by Boldo and Melquiond (2008) the result equals direct rounding."""
+    return f32_to_bf16_rne(f64_to_f32_round_to_odd(x))
+
+
+def ulp_bf16(bits) -> np.ndarray:
+    """Unit in the last place of a bf16 value: 2^(e - 7) for exponent e,
+    2^-133 in the subnormal range and at zero."""
+    b = np.asarray(bits, dtype=np.uint16).astype(np.int64)
+    e = (b >> 7) & 0xFF
+    return np.ldexp(1.0, np.maximum(e, 1) - 127 - 7)
+
+
+# ----------------------------------------------------------------------------
+# The projection.
+# ----------------------------------------------------------------------------
+
+
+def dot_f64(h_bits, w_bits):
+    """S[m, v] = sum_k h[m, k] * w[v, k] and A[m, v] = sum_k |h[m, k] * w[v, k]|,
+    both in binary64. Every bf16 x bf16 product is exact in binary64, so the
+    only rounding is that of the binary64 sums (relative 2^-53 per add)."""
+    hf = bf16_to_f64(h_bits)
+    wf = bf16_to_f64(w_bits)
+    return _dot_pair(hf, wf)
+
+
+def _dot_pair(hf, wf):
+    S = hf @ wf.T
+    A = np.abs(hf) @ np.abs(wf).T
+    return S, A
+
+
+def logits_f32(S, alpha: float, bias=None) -> np.ndarray:
+    """fp32 logits from binary64 dot products, in the unfused order: round the
+    projection to fp32, multiply by alpha in fp32, then add the fp32 bias in
+    fp32 (no fused multiply-add)."""
+    a = np.float32(alpha)
+    r = np.asarray(S, dtype=np.float64).astype(np.float32)
+    r = (r * a).astype(np.float32)
+    if bias is not None:
+        r = (r + np.asarray(bias, dtype=np.float32)).astype(np.float32)
+    return r
+
+
+def logits_bf16(S, alpha: float, bias=None) -> np.ndarray:
+    """bf16 logits (bits): alpha*S (+ bias) in binary64, correctly rounded."""
+    y = np.float64(np.float32(alpha)) * np.asarray(S, dtype=np.float64)
+    if bias is not None:
+        y = y + np.asarray(bias, dtype=np.float32).astype(np.float64)
+    return f64_to_bf16_correct(y)
+
+
+def lmhead_logits(h_bits, w_bits, alpha: float, bias=None, out_dtype: str = "f32"):
+    """Reference logits for bf16 hidden [M, H] and bf16 weight [V, H].
+
+    Returns (logits, A): logits are fp32 values for out_dtype "f32" or bf16 bit
+    patterns (uint16) for "bf16"; A = sum_k |h*w| for the tolerance."""
+    S, A = dot_f64(h_bits, w_bits)
+    if out_dtype == "f32":
+        return logits_f32(S, alpha, bias), A
+    if out_dtype == "bf16":
+        return logits_bf16(S, alpha, bias), A
+    raise ValueError(out_dtype)
+
+
+def lmhead_logits_nvfp4(h_bits, packed, scale_bytes, g: float, alpha: float = 1.0, bias=None):
+    """Reference bf16 logits (bits) of the W4A16 NVFP4 head, and A for the
+    tolerance: y = g * alpha * S (+ bias) in binary64 with S the exact-product
+    binary64 dot of the bf16 hidden with the dequantised weight, correctly
+    rounded to bf16. g and alpha are taken at their binary32 values."""
+    hf = bf16_to_f64(h_bits)
+    H = hf.shape[-1]
+    wf = nvfp4_weight_f64(packed, scale_bytes, H)
+    S, A = _dot_pair(hf, wf)
+    ga = np.float64(np.float32(g)) * np.float64(np.float32(alpha))
+    y = ga * S
+    if bias is not None:
+        y = y + np.asarray(bias, dtype=np.float32).astype(np.float64)
+    return f64_to_bf16_correct(y), A

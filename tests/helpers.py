@@ -1,0 +1,117 @@
+"""Shared test helpers: golden-file parsing, exact rational rounding and the
+parity tolerances. Nothing here computes logits."""
+from __future__ import annotations
+
+from fractions import Fraction
+from pathlib import Path
+
+import numpy as np
+
+ROOT = Path(__file__).resolve().parents[1]
+
+
+def load_golden(name):
+    """Parse a tests/golden fixture: '#' comments; 'key v1 v2 ...' lines; a
+    repeated key gives one list per line."""
+    out = {}
+    for line in (ROOT / "tests" / "golden" / name).read_text().splitlines():
+        line = line.split("#", 1)[0].strip()
+        if not line:
+            continue
+        key, *vals = line.split()
+        out.setdefault(key, []).append(vals)
+    return out
+
+
+def num(s: str) -> float:
+    return float(int(s, 16)) if s.lower().startswith("0x") else float(s)
+
+
+def f32_bits_to_bf16_bits_exact(values) -> np.ndarray:
+    """bf16 bits of values that are exactly representable in bf16 (asserted)."""
+    f = np.asarray(values, dtype=np.float32)
+    u = f.view(np.uint32)
+    assert np.all((u & 0xFFFF) == 0), "value not exact in bf16"
+    return (u >> 16).astype(np.uint16)
+
+
+# ---------------------------------------------------------------------------
+# Exact rational rounding to a binary format (round to nearest, ties to even),
+# written from the IEEE 754 definition with integer arithmetic only.
+# ---------------------------------------------------------------------------
+
+def _floor_log2(a: Fraction) -> int:
+    e = a.numerator.bit_length() - a.denominator.bit_length()
+    while Fraction(2) ** e > a:
+        e -= 1
+    while Fraction(2) ** (e + 1) <= a:
+        e += 1
+    return e
+
+
+def round_fraction(q: Fraction, p: int, emin: int) -> Fraction:
+    """Nearest-even rounding of q to p significand bits, minimum normal
+    exponent emin (gradual underflow below it). No overflow handling."""
+    if q == 0:
+        return Fraction(0)
+    sign = -1 if q < 0 else 1
+    a = abs(q)
+    e = max(_floor_log2(a), emin)
+    quantum = Fraction(2) ** (e - p + 1)
+    n = a / quantum
+    fl = n.numerator // n.denominator
+    rem = n - fl
+    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and fl % 2 == 1):
+        fl += 1
+    return sign * fl * quantum
+
+
+def rne32(q: Fraction) -> Fraction:
+    return round_fraction(q, 24, -126)
+
+
+def rne_bf16(q: Fraction) -> Fraction:
+    return round_fraction(q, 8, -126)
+
+
+# ---------------------------------------------------------------------------
+# Parity tolerances.
+# ---------------------------------------------------------------------------
+
+def check_f32(gpu, ref, A, rel=2e-5, what=""):
+    """|gpu - ref| <= rel * A + 1e-30 per element; returns (max ratio, exact fraction)."""
+    gpu = np.asarray(gpu, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    bound = rel * np.asarray(A, dtype=np.float64) + 1e-30
+    err = np.abs(gpu - ref)
+    bad = ~(err <= bound)
+    if bad.any():
+        idx = np.argwhere(bad)[:5]
+        raise AssertionError(f"{what}: {int(bad.sum())} elements out of tolerance, e.g. "
+                             + ", ".join(f"{tuple(i)}: gpu={gpu[tuple(i)]!r} ref={ref[tuple(i)]!r} "
+                                         f"bound={bound[tuple(i)]:.3g}" for i in idx))
+    return float(np.max(err / bound)) if err.size else 0.0, float(np.mean(err == 0)) if err.size else 1.0
+
+
+def bf16_bits_to_f64(bits):
+    b = np.asarray(bits, dtype=np.uint16)
+    return (b.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def check_bf16(gpu_bits, ref_bits, A, scale, ulp_fn, rel=2e-5, what=""):
+    """bf16 parity: |gpu - ref| <= max(1 ulp(ref), rel*|scale|*A) per element
+    (the second term covers cancellation near zero, where one bf16 ulp is
+    smaller than any fp32-accumulation error). Returns the number of elements
+    outside the strict 1-ulp bound, which the caller may report."""
+    g = bf16_bits_to_f64(gpu_bits)
+    r = bf16_bits_to_f64(ref_bits)
+    ulp = ulp_fn(ref_bits)
+    err = np.abs(g - r)
+    bound = np.maximum(ulp, rel * abs(scale) * np.asarray(A, dtype=np.float64))
+    bad = ~(err <= bound)
+    if bad.any():
+        idx = np.argwhere(bad)[:5]
+        raise AssertionError(f"{what}: {int(bad.sum())} bf16 elements out of tolerance, e.g. "
+                             + ", ".join(f"{tuple(i)}: gpu={g[tuple(i)]!r} ref={r[tuple(i)]!r}"
+                                         for i in idx))
+    return int(np.sum(err > ulp))
