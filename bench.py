@@ -1,0 +1,303 @@
+#!/usr/bin/env python3
+"""Benchmark of the LM-head logits library on one MI355X.
+
+A step is one pass of the hot path over the decode workload (H=4096,
+V=128256, bf16 weight ~N(0, 0.02), hidden ~N(0, 1), fp32 logits, alpha=1/16):
+one lmhead_logits call for each M in {1, 2, 8, 32, 64}. The headline value is
+the whole step's algorithmic HBM throughput (weight read once + hidden +
+output written, divided by the step time). The other workloads -- prefill
+(M=2048), spec-decode (M=128 with bias) and the NVFP4 head (M in 1, 16, 64,
+256) -- are timed after it and reported alongside.
+
+Inputs are generated on the host from the seeded generator, copied to HBM
+before timing, and never touched by the timed region. Timing uses HIP events
+on the stream the library launches on (torch's current stream).
+
+Output: one JSON line on stdout.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+from pathlib import Path
+
+ROOT = Path(__file__).resolve().parent
+sys.path.insert(0, str(ROOT))
+
+import numpy as np  # noqa: E402
+
+HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2516.6       # MI355X dense bf16 MFMA (256 CU x 4096 FLOP/clk x 2.4 GHz)
+METRIC = ("LM-head µs/call + HBM GB/s (M≤64) and TFLOP/s (M=2048), % of roofline")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+# ----------------------------------------------------------------------------
+# Algorithmic byte and flop models (W read once + hidden + bias + output).
+# ----------------------------------------------------------------------------
+
+def bytes_bf16(M, H, V, out_bytes, bias):
+    return V * H * 2 + M * H * 2 + (V * 4 if bias else 0) + M * V * out_bytes
+
+
+def bytes_nvfp4(M, H, V, bias=False):
+    return V * H // 2 + V * H // 16 + M * H * 2 + (V * 4 if bias else 0) + M * V * 2
+
+
+def flops(M, H, V):
+    return 2 * M * H * V
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for p in sorted((ROOT / "lm_head_logits_amd" / "csrc").glob("*")):
+        h.update(p.name.encode())
+        h.update(p.read_bytes())
+    return h.hexdigest()[:16]
+
+
+def committed_traffic(kernel: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
+    was taken on the current kernel sources; else None."""
+    f = ROOT / "profiles" / "traffic_counters.md"
+    if not f.exists():
+        return None
+    text = f.read_text()
+    m = re.search(r"source-hash:\s*([0-9a-f]+)", text)
+    if not m or m.group(1) != kernel_source_hash():
+        return None
+    m = re.search(rf"^\|\s*{re.escape(kernel)}\s*\|[^\n]*?\|\s*([0-9.]+)\s*\|\s*$", text, re.M)
+    return float(m.group(1)) if m else None
+
+
+# ----------------------------------------------------------------------------
+# GPU timing
+# ----------------------------------------------------------------------------
+
+def timed_calls(torch, fns, warmup, steps):
+    """Run `fns` (one step = each fn once) warmup + steps times. Returns the
+    step wall time (ms, events around all steps) and per-fn average launch
+    time in ms (events around each call)."""
+    for _ in range(warmup):
+        for f in fns:
+            f()
+    torch.cuda.synchronize()
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in fns] for _ in range(steps)]
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t0.record()
+    for s in range(steps):
+        for i, f in enumerate(fns):
+            ev[s][i][0].record()
+            f()
+            ev[s][i][1].record()
+    t1.record()
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - wall0) * 1e3
+    total = t0.elapsed_time(t1)
+    per = [[ev[s][i][0].elapsed_time(ev[s][i][1]) for s in range(steps)] for i in range(len(fns))]
+    return total / steps, wall / steps, per
+
+
+def to_dev_bf16(torch, a, dev):
+    return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+
+
+def bench_decode(torch, L, wl, dev, warmup, steps):
+    w = wl.DECODE
+    log("decode: generating inputs")
+    h, W = wl.hidden(w), wl.weight(w)
+    hd, Wd = to_dev_bf16(torch, h, dev), to_dev_bf16(torch, W, dev)
+    alpha = w.alphas[1]
+    outs = {M: torch.empty((M, w.V), dtype=torch.float32, device=dev) for M in w.Ms}
+    fns = [(lambda M=M: L.logits(hd[:M], Wd, alpha, None, torch.float32, out=outs[M])) for M in w.Ms]
+    step_ms, wall_ms, per = timed_calls(torch, fns, warmup, steps)
+    per_m = {}
+    tot_bytes = 0
+    for M, ts in zip(w.Ms, per):
+        b = bytes_bf16(M, w.H, w.V, 4, False)
+        tot_bytes += b
+        us_avg = 1e3 * float(np.mean(ts))
+        per_m[str(M)] = {"us_avg": round(us_avg, 2), "us_min": round(1e3 * float(np.min(ts)), 2),
+                         "GBps": round(b / us_avg / 1e3, 1),
+                         "frac_hbm": round(b / us_avg / 1e3 / HBM_PEAK_GBPS, 4),
+                         "roofline_us": round(b / HBM_PEAK_GBPS / 1e3, 2)}
+    launches_ms = float(np.sum([np.mean(ts) for ts in per]))
+    return {"w": w, "per_m": per_m, "step_ms": step_ms, "wall_ms": wall_ms,
+            "bytes_per_step": tot_bytes, "launch_ms_sum": launches_ms, "h": h, "W": W}
+
+
+def bench_prefill(torch, L, wl, dev, warmup, steps):
+    w = wl.PREFILL
+    log("prefill: generating inputs")
+    h, W = wl.hidden(w), wl.weight(w)
+    hd, Wd = to_dev_bf16(torch, h, dev), to_dev_bf16(torch, W, dev)
+    out = torch.empty((w.M, w.V), dtype=torch.float32, device=dev)
+    step_ms, _, per = timed_calls(torch, [lambda: L.logits(hd, Wd, w.alphas[0], None, out=out)],
+                                  warmup, steps)
+    us = 1e3 * float(np.mean(per[0]))
+    f = flops(w.M, w.H, w.V)
+    del hd, Wd, out
+    return {"M": w.M, "H": w.H, "V": w.V, "us_avg": round(us, 1),
+            "us_min": round(1e3 * float(np.min(per[0])), 1),
+            "TFLOPs": round(f / us / 1e6, 1), "frac_mfma": round(f / us / 1e6 / BF16_PEAK_TFLOPS, 4),
+            "roofline_us": round(max(f / BF16_PEAK_TFLOPS / 1e6,
+                                     bytes_bf16(w.M, w.H, w.V, 4, False) / HBM_PEAK_GBPS / 1e3), 1)}
+
+
+def bench_spec(torch, L, wl, dev, warmup, steps):
+    w = wl.SPEC
+    log("spec: generating inputs")
+    h, W, b = wl.hidden(w), wl.weight(w), wl.bias(w)
+    hd, Wd = to_dev_bf16(torch, h, dev), to_dev_bf16(torch, W, dev)
+    bd = torch.from_numpy(b).to(dev)
+    res = {}
+    for M in (w.M, 32):
+        out = torch.empty((M, w.V), dtype=torch.float32, device=dev)
+        _, _, per = timed_calls(torch, [lambda: L.logits(hd[:M], Wd, w.alphas[0], bd, out=out)],
+                                warmup, steps)
+        us = 1e3 * float(np.mean(per[0]))
+        by = bytes_bf16(M, w.H, w.V, 4, True)
+        res[str(M)] = {"us_avg": round(us, 2), "GBps": round(by / us / 1e3, 1),
+                       "frac_hbm": round(by / us / 1e3 / HBM_PEAK_GBPS, 4),
+                       "roofline_us": round(by / HBM_PEAK_GBPS / 1e3, 2)}
+    return res
+
+
+def bench_nvfp4(torch, L, wl, dev, warmup, steps, copies=4):
+    w = wl.NVFP4
+    log("nvfp4: generating inputs")
+    h, c, s = wl.hidden(w), wl.codes(w), wl.scales(w)
+    hd = to_dev_bf16(torch, h, dev)
+    # several copies of the 175 MB head so successive calls cannot hit the 256 MB MALL
+    cs = [torch.from_numpy(c).to(dev) for _ in range(copies)]
+    ss = [torch.from_numpy(s).to(dev) for _ in range(copies)]
+    res = {}
+    for M in w.Ms:
+        out = torch.empty((M, w.V), dtype=torch.bfloat16, device=dev)
+        fns = [(lambda i=i: L.logits_nvfp4(hd[:M], cs[i], ss[i], w.g, 1.0, out=out))
+               for i in range(copies)]
+        _, _, per = timed_calls(torch, fns, warmup, steps)
+        us = 1e3 * float(np.mean(per))
+        by = bytes_nvfp4(M, w.H, w.V)
+        f = flops(M, w.H, w.V)
+        roof = max(by / HBM_PEAK_GBPS / 1e3, f / BF16_PEAK_TFLOPS / 1e6)
+        res[str(M)] = {"us_avg": round(us, 2), "GBps": round(by / us / 1e3, 1),
+                       "TFLOPs": round(f / us / 1e6, 1), "roofline_us": round(roof, 2),
+                       "frac_roofline": round(roof / us, 4)}
+    return res
+
+
+# ----------------------------------------------------------------------------
+# CPU baseline: the oracle on a bounded sample of the decode workload.
+# ----------------------------------------------------------------------------
+
+def cpu_baseline(wl, h, W, budget_s=12.0):
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = os.cpu_count() or 1
+    w = wl.DECODE
+    M = 64
+    # grow the vocabulary slice until one oracle call takes a few seconds
+    nv = 1024
+    while True:
+        t0 = time.perf_counter()
+        oracle.lmhead_logits(h[:M], W[:nv], w.alphas[1], None, "f32")
+        dt = time.perf_counter() - t0
+        if dt > budget_s / 4 or nv >= w.V:
+            break
+        nv = min(w.V, nv * 4)
+    reps, t_total = 0, 0.0
+    while t_total < budget_s * 0.75 and reps < 5:
+        t0 = time.perf_counter()
+        oracle.lmhead_logits(h[:M], W[:nv], w.alphas[1], None, "f32")
+        t_total += time.perf_counter() - t0
+        reps += 1
+    per_call = t_total / reps
+    b = nv * w.H * 2 + M * w.H * 2 + M * nv * 4
+    return {"value": round(b / per_call / 1e9, 3), "unit": "GB/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"decode head M=64, first {nv} of {w.V} vocabulary rows, H={w.H}, fp32 out; "
+                      f"{reps} calls, {per_call:.2f} s each (numpy fp64 oracle)",
+            "us_per_call_full_vocab_est": round(per_call * w.V / nv * 1e6, 0)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--only", choices=["decode", "all"], default="all",
+                    help="decode: the headline step only (for profiling)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this library shards by vocabulary with no exchange, "
+              "and multi-GPU runs are not part of this build. Use --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import lm_head_logits_amd as L
+    import synth.workloads as wl
+
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    dec = bench_decode(torch, L, wl, dev, args.warmup, args.steps)
+    extra = {}
+    if args.only == "all":
+        extra["prefill"] = bench_prefill(torch, L, wl, dev, args.warmup, max(5, args.steps // 5))
+        torch.cuda.empty_cache()
+        extra["spec_decode"] = bench_spec(torch, L, wl, dev, args.warmup, args.steps)
+        torch.cuda.empty_cache()
+        extra["nvfp4"] = bench_nvfp4(torch, L, wl, dev, args.warmup, args.steps)
+
+    w = dec["w"]
+    step_ms = dec["step_ms"]
+    value = dec["bytes_per_step"] / (step_ms * 1e-3) / 1e9
+    launches = len(w.Ms)
+    achieved = dec["bytes_per_step"] / launches / (dec["launch_ms_sum"] / launches * 1e-3) / 1e9
+    traffic = committed_traffic("skinny_decode")
+    line = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded SplitMix64/Box-Muller inputs of the workload's shapes)",
+        "config": {"workload": "decode head: H=4096, V=128256, bf16 W ~N(0,0.02), bf16 hidden "
+                               "~N(0,1), alpha=1/16, fp32 out; one step = one call at each M in "
+                               "{1,2,8,32,64}",
+                   "H": w.H, "V": w.V, "Ms": list(w.Ms), "parallelism": "none (1 GPU)"},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                     "traffic": traffic, "kernel": "skinny_kernel (decode, M<=64)"},
+        "decode_per_M": dec["per_m"],
+        **extra,
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(wl, dec["h"], dec["W"])
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,147 @@
+/*
+ * lmhead.h -- C ABI of the MI355X (gfx950) LM-head logits library.
+ *
+ *   logits[m, v] = alpha * (hidden[m, :] . W[v, :]) + bias[v]
+ *
+ * bf16 inputs, fp32 accumulation, fp32 or bf16 output; an NVFP4 weight-only
+ * (W4A16) variant with bf16 output. Every output row depends only on its own
+ * hidden row, the weight, alpha, bias and the output type: never on how many
+ * rows are in the call, where the row sits in it, or which entry point (bf16
+ * weight at any M) produced it.
+ *
+ * Where the operation is defined (page title, then section):
+ *  - bf16 x bf16 products accumulated at fp32 with fp32 logits and no fp32
+ *    copy of the weight: sglang PR 32370 digest "FP32 LM head skips the FP32
+ *    cast" (motivation; implementation breakdown; key source excerpt of
+ *    _compute_lm_head), and vLLM PR 49120 "Honor fp32 head_dtype in Inkling
+ *    muP logits (target + MTP draft)", section Purpose.
+ *  - alpha = 1/mup folded into the projection's epilogue, equal bit for bit
+ *    to the projection followed by a separate multiply: vLLM PR 49120,
+ *    sections Purpose and "muP is folded into the fp32 GEMM (not a bypass)".
+ *  - the embedding bias added to the logits: sglang digest, _compute_lm_head
+ *    excerpt (embedding_bias argument).
+ *  - the NVFP4 head with 16-bit activations and bf16 logits, whose rows do
+ *    not depend on the row count, run in calls of at most 64 rows: metrale
+ *    "lm_head_nvfp4_rows.rs" source page, module documentation and the row
+ *    loop of lm_head_nvfp4_rows_run.
+ *  - "launch nothing and report that the fast path does not cover the case",
+ *    leaving the caller to fall back: the same metrale page (the Ok(false)
+ *    return of lm_head_nvfp4_rows_run) and vLLM PR 49120, section Purpose
+ *    (fallback cases the fused op does not cover).
+ *
+ * Conventions shared by every entry point:
+ *  - Every tensor pointer is a DEVICE pointer to memory the caller owns and
+ *    keeps alive until the enqueued work has finished. The library never
+ *    allocates, frees or synchronises; it only enqueues kernels on `stream`.
+ *  - All tensors are dense and row-major: hidden [M, H], W [V, H] (the
+ *    nn.Linear layout, used transposed), logits [M, V].
+ *  - `stream` is a hipStream_t passed as void*; NULL means the default stream.
+ *  - `out` must not overlap any input.
+ *  - Work is checked on the host before anything is launched; on any non-OK
+ *    status nothing was launched. Faults inside a kernel surface at the
+ *    caller's next synchronisation, as for any HIP work.
+ *  - The library keeps no state between calls apart from HIP's own
+ *    once-per-process code-object load; calls from several threads are safe.
+ */
+#ifndef LMHEAD_H
+#define LMHEAD_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  LMHEAD_F32 = 0,  /* fp32 logits, 4 bytes per element */
+  LMHEAD_BF16 = 1  /* bf16 logits (round to nearest even), 2 bytes per element */
+} lmhead_dtype;
+
+typedef enum {
+  LMHEAD_OK = 0,           /* work enqueued on `stream`, or M == 0 and nothing to do */
+  LMHEAD_NOT_HANDLED = 1,  /* well-formed, outside the shape contract: nothing launched,
+                              the caller falls back */
+  LMHEAD_ERR_INVALID = -1, /* NULL pointer with M > 0, M < 0, H <= 0, V <= 0, unknown dtype
+                              or path, sizes beyond the documented maxima */
+  LMHEAD_ERR_ALIGN = -2,   /* a base pointer below its required alignment */
+  LMHEAD_ERR_DEVICE = -3   /* HIP reported an error when the kernel was launched */
+} lmhead_status;
+
+typedef enum {
+  LMHEAD_PATH_NONE = -1,   /* outside the contract: NOT_HANDLED */
+  LMHEAD_PATH_AUTO = -2,   /* let the library choose (the normal use) */
+  LMHEAD_PATH_SKINNY = 0,  /* weight-streaming split-V kernel, chosen for M <= 64 */
+  LMHEAD_PATH_TILED = 1,   /* LDS-tiled MFMA GEMM, chosen for M > 64 */
+  LMHEAD_PATH_NVFP4 = 2    /* NVFP4 W4A16 kernel */
+} lmhead_path;
+
+/* Shape contract (both entry points):
+ *   M >= 0, H >= 32 and H % 32 == 0, V >= 1,
+ *   M <= LMHEAD_MAX_M, H <= LMHEAD_MAX_H, V <= LMHEAD_MAX_V.
+ * Alignment: hidden, W, w_e2m1 and out 16-byte aligned; bias 4-byte aligned;
+ * w_scale 2-byte aligned. (torch allocations are 256-byte aligned; a row
+ * sub-range W + v0*H stays 16-byte aligned because H % 32 == 0.) */
+#define LMHEAD_MAX_M ((int64_t)1 << 24)
+#define LMHEAD_MAX_H ((int64_t)1 << 16)
+#define LMHEAD_MAX_V ((int64_t)1 << 30)
+
+/* The projection with a bf16 weight.
+ *   hidden    bf16 [M, H]                       (device, read)
+ *   W         bf16 [V, H]                       (device, read)
+ *   alpha     fp32 scale applied to the fp32 accumulator: t = fl32(alpha * acc)
+ *   bias      fp32 [V] or NULL                  (device, read): t = fl32(t + bias[v]),
+ *             a separate rounding, never fused with the multiply
+ *   out_dtype LMHEAD_F32 or LMHEAD_BF16
+ *   out       [M, V] of out_dtype               (device, written; every element)
+ * Returns LMHEAD_OK, LMHEAD_NOT_HANDLED (H % 32 != 0) or an error. */
+lmhead_status lmhead_logits(const void *hidden, int64_t M, int64_t H, const void *W, int64_t V,
+                            float alpha, const float *bias, lmhead_dtype out_dtype, void *out,
+                            void *stream);
+
+/* As lmhead_logits, with the kernel chosen by the caller: LMHEAD_PATH_AUTO,
+ * LMHEAD_PATH_SKINNY (any M; the chunked skinny kernel walks 64-row blocks)
+ * or LMHEAD_PATH_TILED (any M). Both kernels run the same K-step chain, so
+ * their results are bit-identical; this entry point exists to show that. */
+lmhead_status lmhead_logits_path(const void *hidden, int64_t M, int64_t H, const void *W,
+                                 int64_t V, float alpha, const float *bias,
+                                 lmhead_dtype out_dtype, void *out, void *stream, int path);
+
+/* The NVFP4 W4A16 head (bf16 logits).
+ *   hidden       bf16 [M, H]                    (device, read)
+ *   w_e2m1       uint8 [V, H/2]: two OCP E2M1 codes per byte, element 2i in the
+ *                low nibble and 2i+1 in the high nibble (device, read)
+ *   w_scale      uint8 [V, H/16]: one OCP E4M3 scale per 16 consecutive
+ *                elements of a weight row (device, read)
+ *   global_scale fp32 per-tensor scale g
+ *   alpha, bias  as in lmhead_logits; the epilogue multiplies the accumulator
+ *                by s = fl32(global_scale * alpha), then adds the bias
+ *   out          bf16 [M, V]                    (device, written)
+ * The weight w[v, k] = e2m1 * e4m3 is exact in bf16 and runs through the same
+ * K-step chain as lmhead_logits: lmhead_logits_nvfp4 equals lmhead_logits on
+ * the dequantised weight with alpha' = s, bit for bit. */
+lmhead_status lmhead_logits_nvfp4(const void *hidden, int64_t M, int64_t H,
+                                  const uint8_t *w_e2m1, const uint8_t *w_scale,
+                                  float global_scale, int64_t V, float alpha, const float *bias,
+                                  void *out, void *stream);
+
+/* Host-only shape predicate (no device access): 1 when (M, H, V) is inside the
+ * shape contract of the bf16 (nvfp4 = 0) or NVFP4 (nvfp4 = 1) entry point,
+ * else 0. Like the shape check the metrale page's install step runs before
+ * enabling its row-tile head. */
+int lmhead_shape_ok(int64_t M, int64_t H, int64_t V, int nvfp4);
+
+/* Host-only: the lmhead_path the AUTO choice takes for this shape, or
+ * LMHEAD_PATH_NONE when the shape is outside the contract. */
+int lmhead_path_for(int64_t M, int64_t H, int64_t V, int nvfp4);
+
+/* Static, human-readable name of a status code. */
+const char *lmhead_status_string(int status);
+
+/* Library version string, "major.minor.patch". */
+const char *lmhead_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LMHEAD_H */

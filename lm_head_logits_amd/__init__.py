@@ -1,0 +1,134 @@
+"""LM-head logits on MI355X: a thin Python binding over the C ABI of liblmhead.so.
+
+    logits[M, V] = alpha * (hidden[M, H] . W[V, H]^T) + bias[V]
+
+Every step of the projection runs in the library's HIP kernels. This module
+only checks tensor metadata, allocates the output through torch and passes
+device pointers and torch's current HIP stream to the C functions of
+include/lmhead.h. There is no fallback computation: when the library returns
+LMHEAD_NOT_HANDLED the caller gets ``NotHandled`` and decides what to do.
+"""
+from __future__ import annotations
+
+import torch
+
+from . import _lib
+from ._lib import (LMHEAD_BF16, LMHEAD_F32, NOT_HANDLED, OK, PATH_AUTO, PATH_NONE, PATH_NVFP4,
+                   PATH_SKINNY, PATH_TILED)
+
+__all__ = ["logits", "logits_nvfp4", "shape_ok", "path_for", "status_string", "version",
+           "LmHeadError", "NotHandled", "PATH_SKINNY", "PATH_TILED", "PATH_NVFP4", "PATH_AUTO",
+           "PATH_NONE"]
+
+
+class LmHeadError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {status_string(status)} (status {status})")
+
+
+class NotHandled(LmHeadError):
+    """The shape lies outside the kernels' contract; nothing was launched."""
+
+
+def status_string(status: int) -> str:
+    return _lib.load().lmhead_status_string(int(status)).decode()
+
+
+def version() -> str:
+    return _lib.load().lmhead_version().decode()
+
+
+def shape_ok(M: int, H: int, V: int, nvfp4: bool = False) -> bool:
+    return bool(_lib.load().lmhead_shape_ok(M, H, V, int(nvfp4)))
+
+
+def path_for(M: int, H: int, V: int, nvfp4: bool = False) -> int:
+    return int(_lib.load().lmhead_path_for(M, H, V, int(nvfp4)))
+
+
+def _check(status: int, where: str):
+    if status == OK:
+        return
+    if status == NOT_HANDLED:
+        raise NotHandled(status, where)
+    raise LmHeadError(status, where)
+
+
+def _stream_handle(device, stream):
+    s = stream if stream is not None else torch.cuda.current_stream(device)
+    return s.cuda_stream
+
+
+def _need(cond: bool, msg: str):
+    if not cond:
+        raise ValueError(msg)
+
+
+_PATHS = {"auto": PATH_AUTO, "skinny": PATH_SKINNY, "tiled": PATH_TILED}
+
+
+def logits(hidden: torch.Tensor, weight: torch.Tensor, alpha: float = 1.0, bias=None,
+           out_dtype=torch.float32, out: torch.Tensor | None = None, *, path: str = "auto",
+           stream=None) -> torch.Tensor:
+    """alpha * hidden @ weight.T (+ bias): bf16 [M, H] x bf16 [V, H] -> [M, V]
+    fp32 or bf16, accumulated at fp32 (lmhead_logits / lmhead_logits_path)."""
+    _need(hidden.is_cuda and weight.is_cuda, "hidden and weight must be device tensors")
+    _need(hidden.dtype == torch.bfloat16 and weight.dtype == torch.bfloat16,
+          "hidden and weight must be bf16")
+    _need(hidden.dim() == 2 and weight.dim() == 2, "hidden [M, H] and weight [V, H] are 2-D")
+    _need(hidden.is_contiguous() and weight.is_contiguous(), "inputs must be contiguous")
+    M, H = hidden.shape
+    V, H2 = weight.shape
+    _need(H == H2, f"hidden has H={H}, weight has H={H2}")
+    _need(out_dtype in (torch.float32, torch.bfloat16), "out_dtype is float32 or bfloat16")
+    if bias is not None:
+        _need(bias.is_cuda and bias.dtype == torch.float32 and bias.shape == (V,)
+              and bias.is_contiguous(), "bias must be a contiguous fp32 device tensor [V]")
+    if out is None:
+        out = torch.empty((M, V), dtype=out_dtype, device=hidden.device)
+    else:
+        _need(out.is_cuda and out.dtype == out_dtype and out.shape == (M, V) and out.is_contiguous(),
+              "out must be a contiguous [M, V] device tensor of out_dtype")
+    st = _lib.load().lmhead_logits_path(
+        hidden.data_ptr(), M, H, weight.data_ptr(), V, float(alpha),
+        bias.data_ptr() if bias is not None else None,
+        LMHEAD_BF16 if out_dtype == torch.bfloat16 else LMHEAD_F32,
+        out.data_ptr(), _stream_handle(hidden.device, stream), _PATHS[path])
+    _check(st, "lmhead_logits")
+    return out
+
+
+def logits_nvfp4(hidden: torch.Tensor, codes: torch.Tensor, scales: torch.Tensor,
+                 global_scale: float, alpha: float = 1.0, bias=None,
+                 out: torch.Tensor | None = None, *, stream=None) -> torch.Tensor:
+    """NVFP4 W4A16 head: bf16 hidden [M, H], uint8 codes [V, H/2] (two E2M1 per
+    byte, low nibble first), uint8 E4M3 scales [V, H/16], fp32 global scale ->
+    bf16 logits [M, V] (lmhead_logits_nvfp4)."""
+    _need(hidden.is_cuda and codes.is_cuda and scales.is_cuda, "inputs must be device tensors")
+    _need(hidden.dtype == torch.bfloat16, "hidden must be bf16")
+    _need(codes.dtype == torch.uint8 and scales.dtype == torch.uint8, "codes and scales are uint8")
+    _need(hidden.is_contiguous() and codes.is_contiguous() and scales.is_contiguous(),
+          "inputs must be contiguous")
+    M, H = hidden.shape
+    V = codes.shape[0]
+    _need(codes.shape == (V, H // 2) and H % 2 == 0, f"codes must be [V, H/2] = [{V}, {H // 2}]")
+    _need(H % 16 == 0 and scales.shape == (V, H // 16), f"scales must be [V, H/16]")
+    if bias is not None:
+        _need(bias.is_cuda and bias.dtype == torch.float32 and bias.shape == (V,)
+              and bias.is_contiguous(), "bias must be a contiguous fp32 device tensor [V]")
+    if out is None:
+        out = torch.empty((M, V), dtype=torch.bfloat16, device=hidden.device)
+    else:
+        _need(out.is_cuda and out.dtype == torch.bfloat16 and out.shape == (M, V)
+              and out.is_contiguous(), "out must be a contiguous bf16 [M, V] device tensor")
+    st = _lib.load().lmhead_logits_nvfp4(
+        hidden.data_ptr(), M, H, codes.data_ptr(), scales.data_ptr(), float(global_scale), V,
+        float(alpha), bias.data_ptr() if bias is not None else None, out.data_ptr(),
+        _stream_handle(hidden.device, stream))
+    _check(st, "lmhead_logits_nvfp4")
+    return out
+
+
+# Load the HIP library now: a missing or broken build fails the import.
+_lib.load()

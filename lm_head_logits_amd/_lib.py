@@ -1,0 +1,62 @@
+"""ctypes declarations of the C ABI in include/lmhead.h (argument marshalling only).
+
+Loading never falls back to anything: if the HIP library cannot be built or
+loaded, importing fails loudly.
+"""
+from __future__ import annotations
+
+import ctypes
+from pathlib import Path
+
+from . import _build
+
+LMHEAD_F32 = 0
+LMHEAD_BF16 = 1
+
+OK = 0
+NOT_HANDLED = 1
+ERR_INVALID = -1
+ERR_ALIGN = -2
+ERR_DEVICE = -3
+
+PATH_NONE = -1
+PATH_AUTO = -2
+PATH_SKINNY = 0
+PATH_TILED = 1
+PATH_NVFP4 = 2
+
+EXPORTS = ("lmhead_logits", "lmhead_logits_path", "lmhead_logits_nvfp4", "lmhead_shape_ok",
+           "lmhead_path_for", "lmhead_status_string", "lmhead_version")
+
+_lib = None
+
+
+def lib_path() -> Path:
+    return _build.LIB
+
+
+def load() -> ctypes.CDLL:
+    """Load liblmhead.so (building it first only when no build exists)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not _build.LIB.exists():
+        _build.build()
+    lib = ctypes.CDLL(str(_build.LIB))
+    vp, i64, i32, f32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_float
+    lib.lmhead_logits.restype = i32
+    lib.lmhead_logits.argtypes = [vp, i64, i64, vp, i64, f32, vp, i32, vp, vp]
+    lib.lmhead_logits_path.restype = i32
+    lib.lmhead_logits_path.argtypes = [vp, i64, i64, vp, i64, f32, vp, i32, vp, vp, i32]
+    lib.lmhead_logits_nvfp4.restype = i32
+    lib.lmhead_logits_nvfp4.argtypes = [vp, i64, i64, vp, vp, f32, i64, f32, vp, vp, vp]
+    lib.lmhead_shape_ok.restype = i32
+    lib.lmhead_shape_ok.argtypes = [i64, i64, i64, i32]
+    lib.lmhead_path_for.restype = i32
+    lib.lmhead_path_for.argtypes = [i64, i64, i64, i32]
+    lib.lmhead_status_string.restype = ctypes.c_char_p
+    lib.lmhead_status_string.argtypes = [i32]
+    lib.lmhead_version.restype = ctypes.c_char_p
+    lib.lmhead_version.argtypes = []
+    _lib = lib
+    return lib

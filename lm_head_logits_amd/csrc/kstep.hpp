@@ -1,0 +1,84 @@
+// kstep.hpp -- the one K-reduction order every kernel of the library runs.
+//
+// A row's logits must not depend on the row count of the call (metrale
+// "lm_head_nvfp4_rows.rs" source page, module documentation: its row-tile head
+// was chosen over a GEMV/GEMM switch whose summation order changes with the
+// row count). Here every kernel -- the weight-streaming kernel for decode,
+// the LDS-tiled GEMM for prefill and the NVFP4 kernel -- builds each output
+// element with exactly this chain and nothing else:
+//
+//   acc = +0.0f
+//   for k0 = 0, 32, 64, ..., H - 32 (ascending):
+//       acc = MFMA_F32_16x16x32_BF16(acc, h[m, k0 .. k0+31], w[v, k0 .. k0+31])
+//
+// with one fixed placement of the 32 products inside the instruction (the
+// operand map below). There is no split-K, no second accumulator and no
+// cross-lane reduction of partial sums, so the bits of (m, v) depend only on
+// hidden row m and weight row v: not on M, on the 16-row block or row slot the
+// row lands in, or on which kernel ran.
+//
+// Operand map of one K-step (16 x 16 output block at rows r0.., cols c0..):
+//   lane l = 16*g + i  (i = l % 16, g = l / 16)
+//   A operand, slot s (0..7): hidden[r0 + i][k0 + 8*g + s]
+//   B operand, slot s (0..7): W     [c0 + i][k0 + 8*g + s]
+//   accumulator register j : output (r0 + 4*g + j, c0 + i)
+// so each lane feeds 16 contiguous bytes of one hidden row and of one weight
+// row per K-step.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace lmhead {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int KSTEP = 32;  // K consumed by one MFMA
+
+// One step of the chain: acc += A(16 x 32) * B(32 x 16), bf16 in, fp32 out.
+__device__ __forceinline__ f32x4 kstep(f32x4 acc, u32x4 a, u32x4 b) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                 __builtin_bit_cast(bf16x8, b), acc, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x4 zero4() { return f32x4{0.0f, 0.0f, 0.0f, 0.0f}; }
+
+// ---------------------------------------------------------------------------
+// The epilogue (fp32): t = fl32(alpha * acc); with a bias t = fl32(t + b).
+// Two separately rounded operations -- the same bits as the projection
+// followed by an elementwise multiply and then an add (vLLM PR 49120, sections
+// Purpose and "muP is folded into the fp32 GEMM"). __fmul_rn / __fadd_rn keep
+// the compiler from contracting them into one fused multiply-add.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float epilogue(float acc, float alpha, const float *__restrict__ bias,
+                                          int64_t col) {
+  float t = __fmul_rn(alpha, acc);
+  if (bias != nullptr) t = __fadd_rn(t, bias[col]);
+  return t;
+}
+
+// fp32 -> bf16 bits, round to nearest even; NaN stays a quiet NaN.
+__device__ __forceinline__ uint16_t bf16_rne(float f) {
+  uint32_t u = __builtin_bit_cast(uint32_t, f);
+  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (uint16_t)((u >> 16) | 0x40u);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+template <typename OutT>
+__device__ __forceinline__ void store_out(OutT *out, int64_t idx, float t);
+
+template <>
+__device__ __forceinline__ void store_out<float>(float *out, int64_t idx, float t) {
+  out[idx] = t;
+}
+
+template <>
+__device__ __forceinline__ void store_out<uint16_t>(uint16_t *out, int64_t idx, float t) {
+  out[idx] = bf16_rne(t);
+}
+
+}  // namespace lmhead

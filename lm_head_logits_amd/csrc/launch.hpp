@@ -1,0 +1,36 @@
+// launch.hpp -- host-side launchers of the library's kernels (internal).
+// Shapes and alignment are validated by the C ABI before any of these runs.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace lmhead {
+
+struct Bf16Args {
+  const uint16_t *hidden;  // [M, H] bf16
+  int64_t M, H;
+  const uint16_t *W;       // [V, H] bf16
+  int64_t V;
+  float alpha;
+  const float *bias;       // [V] or nullptr
+  int out_bf16;            // 0: fp32 out, 1: bf16 out
+  void *out;               // [M, V]
+};
+
+struct Nvfp4Args {
+  const uint16_t *hidden;  // [M, H] bf16
+  int64_t M, H;
+  const uint8_t *codes;    // [V, H/2] packed E2M1
+  const uint8_t *scales;   // [V, H/16] E4M3
+  int64_t V;
+  float scale;             // fl32(global_scale * alpha)
+  const float *bias;       // [V] or nullptr
+  uint16_t *out;           // [M, V] bf16
+};
+
+hipError_t launch_skinny(const Bf16Args &a, hipStream_t stream);
+hipError_t launch_tiled(const Bf16Args &a, hipStream_t stream);
+hipError_t launch_nvfp4(const Nvfp4Args &a, hipStream_t stream);
+
+}  // namespace lmhead

@@ -1,0 +1,122 @@
+// lmhead_api.cpp -- the C ABI: argument checks, path choice, launch.
+//
+// Every check is host-side integer work done before anything is enqueued; a
+// call that fails one launches nothing (metrale "lm_head_nvfp4_rows.rs"
+// page: its row-tile head returns false and launches nothing when it does not
+// apply; vLLM PR 49120, section Purpose: cases the fused op does not cover
+// fall back). The shape predicates never touch the device.
+#include "../../include/lmhead.h"
+
+#include <hip/hip_runtime.h>
+
+#include "launch.hpp"
+
+namespace {
+
+constexpr int64_t MAX_MV = (int64_t)1 << 42;  // M * V bound: keeps every grid < 2^31 blocks
+
+bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// Contract shared by both entry points; returns LMHEAD_OK when the shape is in.
+lmhead_status check_shape(int64_t M, int64_t H, int64_t V) {
+  if (M < 0 || H <= 0 || V <= 0) return LMHEAD_ERR_INVALID;
+  if (M > LMHEAD_MAX_M || H > LMHEAD_MAX_H || V > LMHEAD_MAX_V) return LMHEAD_ERR_INVALID;
+  if (M > 0 && M > MAX_MV / V) return LMHEAD_ERR_INVALID;
+  if (H % 32 != 0) return LMHEAD_NOT_HANDLED;  // one K-step consumes 32 elements
+  return LMHEAD_OK;
+}
+
+int auto_path(int64_t M) { return M <= 64 ? LMHEAD_PATH_SKINNY : LMHEAD_PATH_TILED; }
+
+}  // namespace
+
+extern "C" {
+
+int lmhead_shape_ok(int64_t M, int64_t H, int64_t V, int nvfp4) {
+  (void)nvfp4;  // both entry points share one shape contract
+  return check_shape(M, H, V) == LMHEAD_OK ? 1 : 0;
+}
+
+int lmhead_path_for(int64_t M, int64_t H, int64_t V, int nvfp4) {
+  if (!lmhead_shape_ok(M, H, V, nvfp4)) return LMHEAD_PATH_NONE;
+  return nvfp4 ? LMHEAD_PATH_NVFP4 : auto_path(M);
+}
+
+const char *lmhead_status_string(int status) {
+  switch (status) {
+    case LMHEAD_OK: return "ok";
+    case LMHEAD_NOT_HANDLED: return "not handled: shape outside the kernels' contract (caller falls back)";
+    case LMHEAD_ERR_INVALID: return "invalid argument";
+    case LMHEAD_ERR_ALIGN: return "misaligned pointer";
+    case LMHEAD_ERR_DEVICE: return "HIP launch error";
+    default: return "unknown status";
+  }
+}
+
+const char *lmhead_version(void) { return "0.1.0"; }
+
+lmhead_status lmhead_logits_path(const void *hidden, int64_t M, int64_t H, const void *W,
+                                 int64_t V, float alpha, const float *bias,
+                                 lmhead_dtype out_dtype, void *out, void *stream, int path) {
+  lmhead_status st = check_shape(M, H, V);
+  if (st != LMHEAD_OK) return st;
+  if (out_dtype != LMHEAD_F32 && out_dtype != LMHEAD_BF16) return LMHEAD_ERR_INVALID;
+  if (path != LMHEAD_PATH_AUTO && path != LMHEAD_PATH_SKINNY && path != LMHEAD_PATH_TILED)
+    return LMHEAD_ERR_INVALID;
+  if (M == 0) return LMHEAD_OK;  // nothing to do, nothing launched
+  if (hidden == nullptr || W == nullptr || out == nullptr) return LMHEAD_ERR_INVALID;
+  if (!aligned(hidden, 16) || !aligned(W, 16) || !aligned(out, 16) ||
+      (bias != nullptr && !aligned(bias, 4)))
+    return LMHEAD_ERR_ALIGN;
+
+  lmhead::Bf16Args a;
+  a.hidden = static_cast<const uint16_t *>(hidden);
+  a.M = M;
+  a.H = H;
+  a.W = static_cast<const uint16_t *>(W);
+  a.V = V;
+  a.alpha = alpha;
+  a.bias = bias;
+  a.out_bf16 = out_dtype == LMHEAD_BF16 ? 1 : 0;
+  a.out = out;
+  const int p = path == LMHEAD_PATH_AUTO ? auto_path(M) : path;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = p == LMHEAD_PATH_SKINNY ? lmhead::launch_skinny(a, s) : lmhead::launch_tiled(a, s);
+  return e == hipSuccess ? LMHEAD_OK : LMHEAD_ERR_DEVICE;
+}
+
+lmhead_status lmhead_logits(const void *hidden, int64_t M, int64_t H, const void *W, int64_t V,
+                            float alpha, const float *bias, lmhead_dtype out_dtype, void *out,
+                            void *stream) {
+  return lmhead_logits_path(hidden, M, H, W, V, alpha, bias, out_dtype, out, stream,
+                            LMHEAD_PATH_AUTO);
+}
+
+lmhead_status lmhead_logits_nvfp4(const void *hidden, int64_t M, int64_t H,
+                                  const uint8_t *w_e2m1, const uint8_t *w_scale,
+                                  float global_scale, int64_t V, float alpha, const float *bias,
+                                  void *out, void *stream) {
+  lmhead_status st = check_shape(M, H, V);
+  if (st != LMHEAD_OK) return st;
+  if (M == 0) return LMHEAD_OK;
+  if (hidden == nullptr || w_e2m1 == nullptr || w_scale == nullptr || out == nullptr)
+    return LMHEAD_ERR_INVALID;
+  if (!aligned(hidden, 16) || !aligned(w_e2m1, 16) || !aligned(w_scale, 2) || !aligned(out, 16) ||
+      (bias != nullptr && !aligned(bias, 4)))
+    return LMHEAD_ERR_ALIGN;
+
+  lmhead::Nvfp4Args a;
+  a.hidden = static_cast<const uint16_t *>(hidden);
+  a.M = M;
+  a.H = H;
+  a.codes = w_e2m1;
+  a.scales = w_scale;
+  a.V = V;
+  a.scale = global_scale * alpha;  // one binary32 multiply, rounded once
+  a.bias = bias;
+  a.out = static_cast<uint16_t *>(out);
+  hipError_t e = lmhead::launch_nvfp4(a, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? LMHEAD_OK : LMHEAD_ERR_DEVICE;
+}
+
+}  // extern "C"

@@ -1,0 +1,106 @@
+"""The C ABI without a GPU: the library loads, exports every function the
+header declares, and rejects bad arguments on the host before touching the
+device (no call here launches anything)."""
+import ctypes
+import re
+
+import pytest
+
+import lm_head_logits_amd as L
+from lm_head_logits_amd import _lib
+from helpers import ROOT
+
+HEADER = ROOT / "include" / "lmhead.h"
+
+
+def declared_functions():
+    text = re.sub(r"/\*.*?\*/", "", HEADER.read_text(), flags=re.S)
+    return sorted(set(re.findall(r"\b(lmhead_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_python_exports():
+    assert declared_functions() == sorted(_lib.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(str(_lib.lib_path()))
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_status_strings_and_version():
+    for s in (0, 1, -1, -2, -3):
+        assert L.status_string(s) and L.status_string(s) != "unknown status"
+    assert L.status_string(99) == "unknown status"
+    assert re.fullmatch(r"\d+\.\d+\.\d+", L.version())
+
+
+@pytest.mark.parametrize("M,H,V,ok", [
+    (1, 4096, 128256, True), (64, 4096, 128256, True), (2048, 4096, 151936, True),
+    (0, 32, 1, True), (5, 32, 1, True),
+    (4, 4016, 4096, False),          # H % 32 != 0: outside the contract
+    (4, 16, 4096, False),
+    (-1, 4096, 10, False), (4, 0, 10, False), (4, 4096, 0, False),
+    ((1 << 24) + 1, 32, 10, False),  # beyond LMHEAD_MAX_M
+    (4, (1 << 16) + 32, 10, False),  # beyond LMHEAD_MAX_H
+    (1 << 24, 32, 1 << 20, False),   # M * V beyond 2^42
+])
+def test_shape_ok(M, H, V, ok):
+    assert L.shape_ok(M, H, V) is ok
+    assert L.shape_ok(M, H, V, nvfp4=True) is ok
+
+
+def test_path_choice():
+    assert L.path_for(1, 4096, 128256) == L.PATH_SKINNY
+    assert L.path_for(64, 4096, 128256) == L.PATH_SKINNY
+    assert L.path_for(65, 4096, 128256) == L.PATH_TILED
+    assert L.path_for(2048, 4096, 151936) == L.PATH_TILED
+    assert L.path_for(256, 2048, 151936, nvfp4=True) == L.PATH_NVFP4
+    assert L.path_for(4, 4016, 4096) == L.PATH_NONE
+
+
+FAKE = 1 << 20  # a 16-byte-aligned non-null address; never dereferenced on these paths
+
+
+def call(hidden=FAKE, M=4, H=64, W=FAKE, V=100, alpha=1.0, bias=None, dt=0, out=FAKE, path=-2):
+    return _lib.load().lmhead_logits_path(hidden, M, H, W, V, alpha, bias, dt, out, None, path)
+
+
+def call4(hidden=FAKE, M=4, H=64, codes=FAKE, scales=FAKE, g=1.0, V=100, alpha=1.0, bias=None,
+          out=FAKE):
+    return _lib.load().lmhead_logits_nvfp4(hidden, M, H, codes, scales, g, V, alpha, bias, out,
+                                           None)
+
+
+def test_m_zero_is_ok_and_launches_nothing():
+    assert call(hidden=None, W=None, out=None, M=0) == _lib.OK
+    assert call4(hidden=None, codes=None, scales=None, out=None, M=0) == _lib.OK
+
+
+def test_invalid_arguments():
+    E = _lib.ERR_INVALID
+    assert call(hidden=None) == E
+    assert call(W=None) == E
+    assert call(out=None) == E
+    assert call(M=-1) == E
+    assert call(H=0) == E
+    assert call(V=0) == E
+    assert call(dt=2) == E
+    assert call(path=7) == E
+    assert call4(codes=None) == E
+    assert call4(scales=None) == E
+
+
+def test_not_handled_shape():
+    assert call(H=48) == _lib.NOT_HANDLED
+    assert call4(H=48) == _lib.NOT_HANDLED
+
+
+def test_alignment():
+    A = _lib.ERR_ALIGN
+    assert call(hidden=FAKE + 8) == A
+    assert call(W=FAKE + 2) == A
+    assert call(out=FAKE + 4) == A
+    assert call(bias=FAKE + 2) == A
+    assert call4(codes=FAKE + 8) == A
+    assert call4(scales=FAKE + 1) == A

@@ -1,0 +1,213 @@
+"""GPU parity on small shapes: hand examples, the tiny workload, ragged and
+degenerate shapes, the epilogue identities and the kernel-to-kernel bit
+identity. Every call goes through the C ABI (via the ctypes binding)."""
+import numpy as np
+import pytest
+import torch
+
+import lm_head_logits_amd as L
+import oracle
+import synth.workloads as wl
+from gpu_util import DEV, bf16_dev, f32_dev, host_bits, host_f32, say, u8_dev
+from helpers import check_bf16, check_f32, f32_bits_to_bf16_bits_exact, load_golden, num
+
+pytestmark = pytest.mark.gpu
+
+PATHS = ("skinny", "tiled")
+
+
+def _rand_bf16(rng, shape, std):
+    return oracle.f32_to_bf16_rne(rng.normal(0, std, shape).astype(np.float32))
+
+
+def _rows(g, key):
+    return np.array([[num(x) for x in row] for row in g[key]], dtype=np.float64)
+
+
+@pytest.mark.parametrize("path", PATHS)
+def test_hand_example_bitwise(path):
+    g = load_golden("hand_2x3x4.txt")
+    say(f"hand 2x3x4 via {path}")
+    alpha = num(g["alpha"][0][0])
+    h = np.zeros((2, 32), dtype=np.uint16)
+    w = np.zeros((3, 32), dtype=np.uint16)
+    h[:, :4] = f32_bits_to_bf16_bits_exact(_rows(g, "hidden"))     # H = 4 zero-padded to one K-step
+    w[:, :4] = f32_bits_to_bf16_bits_exact(_rows(g, "weight"))
+    b = f32_dev(_rows(g, "bias")[0])
+    for bias, key in ((None, "nobias"), (b, "withbias")):
+        want = _rows(g, key).astype(np.float32)
+        o32 = L.logits(bf16_dev(h), bf16_dev(w), alpha, bias, torch.float32, path=path)
+        assert np.array_equal(host_bits(o32), want.view(np.uint32)), key
+        o16 = L.logits(bf16_dev(h), bf16_dev(w), alpha, bias, torch.bfloat16, path=path)
+        assert np.array_equal(host_bits(o16), f32_bits_to_bf16_bits_exact(want)), key
+
+
+@pytest.mark.parametrize("path", PATHS)
+@pytest.mark.parametrize("out", ("f32", "bf16"))
+def test_tiny_workload_parity(path, out):
+    w = wl.TINY
+    say(f"tiny M=4 H=256 V=4096 via {path}, {out} out")
+    h, W = wl.hidden(w), wl.weight(w)
+    alpha = w.alphas[0]
+    ref, A = oracle.lmhead_logits(h, W, alpha, None, out)
+    dt = torch.float32 if out == "f32" else torch.bfloat16
+    got = L.logits(bf16_dev(h), bf16_dev(W), alpha, None, dt, path=path)
+    if out == "f32":
+        check_f32(host_f32(got), ref, A, what="tiny")
+    else:
+        check_bf16(host_bits(got), ref, A, alpha, oracle.ulp_bf16, what="tiny bf16")
+
+
+# (M, H, V): ragged V, one K-step, an odd number of K-steps, the 64-row
+# boundary, ragged M past it, V = 1.
+SHAPES = [(1, 32, 1), (3, 32, 17), (5, 96, 1000), (16, 64, 4111), (63, 160, 333), (64, 128, 257),
+          (65, 96, 129), (130, 224, 515), (200, 32, 2000), (7, 1024, 4097)]
+
+
+@pytest.mark.parametrize("M,H,V", SHAPES)
+def test_ragged_shapes_parity_and_paths_agree(M, H, V):
+    rng = np.random.default_rng(M * 1000 + H + V)
+    say(f"ragged M={M} H={H} V={V}")
+    h = _rand_bf16(rng, (M, H), 1.0)
+    W = _rand_bf16(rng, (V, H), 0.02)
+    bias = rng.normal(0, 0.1, V).astype(np.float32)
+    alpha = 0.125
+    ref, A = oracle.lmhead_logits(h, W, alpha, bias, "f32")
+    hd, Wd, bd = bf16_dev(h), bf16_dev(W), f32_dev(bias)
+    outs = {p: L.logits(hd, Wd, alpha, bd, torch.float32, path=p) for p in PATHS}
+    check_f32(host_f32(outs["skinny"]), ref, A, what="skinny")
+    assert np.array_equal(host_bits(outs["skinny"]), host_bits(outs["tiled"])), \
+        "skinny and tiled kernels must agree bit for bit"
+    auto = L.logits(hd, Wd, alpha, bd, torch.float32)
+    assert np.array_equal(host_bits(auto), host_bits(outs["skinny"]))
+
+
+def test_integer_inputs_are_exact_small():
+    # |partial sums| <= 16 * H < 2^24: every summation order is exact, so the
+    # GPU must equal the oracle bit for bit.
+    M, H, V = 37, 1024, 3001
+    say("integer exact small")
+    h = wl.int_hidden(21, M, H)
+    W = wl.int_weight(21, V, H)
+    for alpha in (1.0, 0.0625):
+        ref, _ = oracle.lmhead_logits(h, W, alpha, None, "f32")
+        for p in PATHS:
+            got = L.logits(bf16_dev(h), bf16_dev(W), alpha, None, torch.float32, path=p)
+            assert np.array_equal(host_bits(got), ref.view(np.uint32)), (p, alpha)
+
+
+@pytest.mark.parametrize("path", PATHS)
+def test_alpha_fold_equals_unfused_multiply(path):
+    rng = np.random.default_rng(5)
+    M, H, V = 48, 512, 3000
+    say(f"alpha fold via {path}")
+    hd = bf16_dev(_rand_bf16(rng, (M, H), 1.0))
+    Wd = bf16_dev(_rand_bf16(rng, (V, H), 0.02))
+    base = L.logits(hd, Wd, 1.0, None, torch.float32, path=path)
+    for a in (1 / 16, 1 / 8, 1 / 4, 1 / 3, 0.7):
+        fused = L.logits(hd, Wd, a, None, torch.float32, path=path)
+        unfused = base * torch.tensor(a, dtype=torch.float32, device=DEV)
+        assert torch.equal(fused.view(torch.int32), unfused.view(torch.int32)), a
+    # bias: a separately rounded add after the scaled projection
+    b = f32_dev(rng.normal(0, 0.1, V))
+    with_b = L.logits(hd, Wd, 0.7, b, torch.float32, path=path)
+    scaled = L.logits(hd, Wd, 0.7, None, torch.float32, path=path)
+    assert torch.equal(with_b.view(torch.int32), (scaled + b).view(torch.int32))
+    # the bf16 output is the fp32 output rounded to nearest even
+    o16 = L.logits(hd, Wd, 0.7, b, torch.bfloat16, path=path)
+    assert np.array_equal(host_bits(o16), oracle.f32_to_bf16_rne(host_f32(with_b)))
+
+
+@pytest.mark.parametrize("path", PATHS)
+def test_zero_hidden_gives_bias_and_one_hot_gathers(path):
+    rng = np.random.default_rng(8)
+    M, H, V = 20, 256, 777
+    say(f"zero hidden / one-hot via {path}")
+    b = rng.normal(0, 0.1, V).astype(np.float32)
+    W = _rand_bf16(rng, (V, H), 0.02)
+    z = L.logits(bf16_dev(np.zeros((M, H), np.uint16)), bf16_dev(W), 0.125, f32_dev(b),
+                 torch.float32, path=path)
+    assert np.array_equal(host_bits(z), np.broadcast_to(b.view(np.uint32), (M, V)))
+    h = _rand_bf16(rng, (M, H), 1.0)
+    ks = rng.integers(0, H, V)
+    onehot = np.zeros((V, H), np.uint16)
+    onehot[np.arange(V), ks] = 0x3F80
+    got = L.logits(bf16_dev(h), bf16_dev(onehot), 0.7, None, torch.float32, path=path)
+    want = (oracle.bf16_to_f64(h).astype(np.float32)[:, ks] * np.float32(0.7)).astype(np.float32)
+    assert np.array_equal(host_bits(got), want.view(np.uint32))
+
+
+def test_m_zero_and_not_handled_launch_nothing():
+    say("M=0 and H%32!=0")
+    Wd = bf16_dev(np.zeros((10, 64), np.uint16))
+    out = L.logits(bf16_dev(np.zeros((0, 64), np.uint16)), Wd)
+    assert out.shape == (0, 10)
+    sentinel = torch.full((3, 10), 7.0, device=DEV)
+    with pytest.raises(L.NotHandled):
+        L.logits(bf16_dev(np.zeros((3, 48), np.uint16)), bf16_dev(np.zeros((10, 48), np.uint16)),
+                 out=sentinel)
+    torch.cuda.synchronize()
+    assert torch.all(sentinel == 7.0)
+
+
+def test_run_to_run_identical():
+    rng = np.random.default_rng(2)
+    say("run to run")
+    hd = bf16_dev(_rand_bf16(rng, (100, 512), 1.0))
+    Wd = bf16_dev(_rand_bf16(rng, (5000, 512), 0.02))
+    for p in PATHS:
+        a = L.logits(hd, Wd, 0.3, None, path=p)
+        b = L.logits(hd, Wd, 0.3, None, path=p)
+        assert torch.equal(a.view(torch.int32), b.view(torch.int32))
+
+
+# ----------------------------------------------------------------------------
+# NVFP4
+# ----------------------------------------------------------------------------
+
+def test_nvfp4_hand_example():
+    g = load_golden("nvfp4_hand.txt")
+    say("nvfp4 hand example")
+    h = f32_bits_to_bf16_bits_exact(_rows(g, "hidden"))
+    codes = np.array([[int(x, 16) for x in row] for row in g["codes"]], dtype=np.uint8)
+    scales = np.array([[int(x, 16) for x in row] for row in g["scales"]], dtype=np.uint8)
+    out = L.logits_nvfp4(bf16_dev(h), u8_dev(codes), u8_dev(scales), num(g["g"][0][0]),
+                         num(g["alpha"][0][0]))
+    want = np.array([[int(x, 16) for x in g["logits_bf16"][0]]], dtype=np.uint16)
+    assert np.array_equal(host_bits(out), want)
+
+
+def test_nvfp4_nibble_order_on_gpu():
+    say("nvfp4 nibble order")
+    codes = np.zeros((2, 16), np.uint8)
+    codes[:, 0] = 0x72                       # element 0 -> 1.0, element 1 -> 6.0
+    scales = np.full((2, 2), 0x38, np.uint8)  # 1.0
+    for e, want in ((0, 0x3F80), (1, 0x40C0)):
+        h = np.zeros((1, 32), np.uint16)
+        h[0, e] = 0x3F80
+        out = L.logits_nvfp4(bf16_dev(h), u8_dev(codes), u8_dev(scales), 1.0)
+        assert host_bits(out)[0, 0] == want
+
+
+@pytest.mark.parametrize("M,H,V", [(1, 32, 1), (4, 64, 100), (64, 256, 1000), (65, 96, 333),
+                                   (200, 512, 2049)])
+def test_nvfp4_parity_and_equals_bf16_path(M, H, V):
+    rng = np.random.default_rng(M + H + V)
+    say(f"nvfp4 M={M} H={H} V={V}")
+    h = _rand_bf16(rng, (M, H), 1.0)
+    codes = rng.integers(0, 256, (V, H // 2), dtype=np.uint8)
+    scales = rng.choice(np.r_[0x30:0x4A], (V, H // 16)).astype(np.uint8)
+    bias = rng.normal(0, 0.1, V).astype(np.float32)
+    g, alpha = 0.01, 0.5
+    for b in (None, bias):
+        ref, A = oracle.lmhead_logits_nvfp4(h, codes, scales, g, alpha, b)
+        bd = f32_dev(b) if b is not None else None
+        got = L.logits_nvfp4(bf16_dev(h), u8_dev(codes), u8_dev(scales), g, alpha, bd)
+        check_bf16(host_bits(got), ref, A, g * alpha, oracle.ulp_bf16, what="nvfp4")
+        # the same chain on the dequantised weight through the bf16 entry point
+        wdeq = oracle.nvfp4_weight_f64(codes, scales, H).astype(np.float32)
+        wbits = f32_bits_to_bf16_bits_exact(wdeq)
+        s = float(np.float32(g) * np.float32(alpha))
+        for p in PATHS:
+            twin = L.logits(bf16_dev(h), bf16_dev(wbits), s, bd, torch.bfloat16, path=p)
+            assert np.array_equal(host_bits(got), host_bits(twin)), p
