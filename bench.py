@@ -241,8 +241,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--only", choices=["decode", "all"], default="all",
-                    help="decode: the headline step only (for profiling)")
+    ap.add_argument("--only", choices=["decode", "prefill", "spec", "nvfp4", "all"], default="all",
+                    help="run one workload only (for profiling); the headline line needs decode")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -256,13 +256,23 @@ def main():
 
     dev = "cuda:0"
     torch.cuda.set_device(0)
-    dec = bench_decode(torch, L, wl, dev, args.warmup, args.steps)
+    run = (lambda name: args.only in (name, "all"))
     extra = {}
-    if args.only == "all":
+    if args.only != "all" and args.only != "decode":
+        # a single non-headline workload, for profiling: print its numbers only
+        fn = {"prefill": lambda: bench_prefill(torch, L, wl, dev, args.warmup, args.steps),
+              "spec": lambda: bench_spec(torch, L, wl, dev, args.warmup, args.steps),
+              "nvfp4": lambda: bench_nvfp4(torch, L, wl, dev, args.warmup, args.steps)}[args.only]
+        print(json.dumps({"workload": args.only, "result": fn()}), flush=True)
+        return
+    dec = bench_decode(torch, L, wl, dev, args.warmup, args.steps)
+    if run("prefill"):
         extra["prefill"] = bench_prefill(torch, L, wl, dev, args.warmup, max(5, args.steps // 5))
         torch.cuda.empty_cache()
+    if run("spec"):
         extra["spec_decode"] = bench_spec(torch, L, wl, dev, args.warmup, args.steps)
         torch.cuda.empty_cache()
+    if run("nvfp4"):
         extra["nvfp4"] = bench_nvfp4(torch, L, wl, dev, args.warmup, args.steps)
 
     w = dec["w"]

@@ -47,6 +47,60 @@ __device__ __forceinline__ f32x4 kstep(f32x4 acc, u32x4 a, u32x4 b) {
 __device__ __forceinline__ f32x4 zero4() { return f32x4{0.0f, 0.0f, 0.0f, 0.0f}; }
 
 // ---------------------------------------------------------------------------
+// Buffer loads. A buffer resource bounds every access: offsets at or past
+// `bytes` read as zero, which is how the kernels fill padding rows and the
+// ragged vocabulary tail without branches. Offsets are 32-bit, so each
+// resource is based at the start of the region one wave or work-group reads.
+// ---------------------------------------------------------------------------
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+
+// Word 3 of a gfx9-family raw (stride 0) buffer resource: 32-bit data format.
+constexpr int RSRC_WORD3 = 0x00020000;
+// Cache-policy bits of a load: nt marks a read-once stream.
+constexpr int LOAD_DEFAULT = 0;
+constexpr int LOAD_STREAM = 2;
+
+// The base and size are wave-uniform by construction; readfirstlane makes the
+// compiler see that too, so the resource lives in scalar registers (a resource
+// it believes divergent turns every load into a loop over lanes).
+__device__ __forceinline__ rsrc_t make_rsrc(const void *base, uint32_t bytes) {
+  const uint64_t b = reinterpret_cast<uint64_t>(base);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)b);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(b >> 32));
+  void *ub = reinterpret_cast<void *>(((uint64_t)hi << 32) | lo);
+  return __builtin_amdgcn_make_buffer_rsrc(ub, (short)0, (int)__builtin_amdgcn_readfirstlane(bytes),
+                                           RSRC_WORD3);
+}
+
+template <int POLICY = LOAD_DEFAULT>
+__device__ __forceinline__ u32x4 load16(rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, POLICY);
+}
+
+template <int POLICY = LOAD_DEFAULT>
+__device__ __forceinline__ uint32_t load4(rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, POLICY);
+}
+
+// Work-group barrier that orders LDS only: waits for this wave's LDS
+// operations, then meets the other waves. Unlike __syncthreads() it does not
+// wait for outstanding global loads, so prefetched weight streams stay in
+// flight across it. The memory clobber keeps the compiler from moving LDS
+// accesses across the barrier.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// Keeps the compiler from moving any instruction across this point. Used
+// before a chunk's hidden rows are written to LDS: hoisting that write above
+// the chunk's MFMAs would make it wait for every load issued since the hidden
+// load (the whole weight prefetch), draining the stream once per chunk.
+__device__ __forceinline__ void sched_fence() {
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("" ::: "memory");
+}
+
+// ---------------------------------------------------------------------------
 // The epilogue (fp32): t = fl32(alpha * acc); with a bias t = fl32(t + b).
 // Two separately rounded operations -- the same bits as the projection
 // followed by an elementwise multiply and then an add (vLLM PR 49120, sections

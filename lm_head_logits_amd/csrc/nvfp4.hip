@@ -14,6 +14,9 @@
 // K-step chain of kstep.hpp runs unchanged. So this kernel's logits equal
 // lmhead_logits on the dequantised weight with alpha = fl32(g * alpha), bit
 // for bit.
+#include <atomic>
+#include <type_traits>
+
 #include "kstep.hpp"
 #include "launch.hpp"
 
@@ -63,7 +66,7 @@ __device__ __forceinline__ u32x4 dequant8(uint32_t codes, float scale) {
 }
 
 template <int R>
-__global__ __launch_bounds__(256) void nvfp4_kernel(const uint16_t *__restrict__ hidden, int64_t M,
+__global__ __launch_bounds__(256) void nvfp4_generic_kernel(const uint16_t *__restrict__ hidden, int64_t M,
                                                     int64_t H, const uint8_t *__restrict__ codes,
                                                     const uint8_t *__restrict__ scales, int64_t V,
                                                     float scale, const float *__restrict__ bias,
@@ -144,24 +147,317 @@ __global__ __launch_bounds__(256) void nvfp4_kernel(const uint16_t *__restrict__
 }
 
 template <int R>
-hipError_t launch_r(const Nvfp4Args &a, hipStream_t stream) {
+hipError_t launch_generic_r(const Nvfp4Args &a, hipStream_t stream) {
   dim3 grid((unsigned)(((a.V + NV_WAVES * NV_NB * 16 - 1) / (NV_WAVES * NV_NB * 16)) *
                        ((a.M + 63) / 64)));
   dim3 block(64 * NV_WAVES);
-  hipLaunchKernelGGL((nvfp4_kernel<R>), grid, block, 0, stream, a.hidden, a.M, a.H, a.codes,
+  hipLaunchKernelGGL((nvfp4_generic_kernel<R>), grid, block, 0, stream, a.hidden, a.M, a.H, a.codes,
                      a.scales, a.V, a.scale, a.bias, a.out);
   return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Streaming kernel for H % 128 == 0 (the common case): the decode-sized
+// NVFP4 head at HBM speed.
+//
+// The K dimension is walked in quads of four K-steps (128 elements: 64 code
+// bytes and 8 scale bytes per weight row). Each lane loads 16 contiguous code
+// bytes -- lane group g takes the codes of the quad's K-step g for all four
+// slot groups -- so a load instruction covers 16 rows x 64 contiguous bytes.
+// A 4 x 4 transpose of 32-bit words across the four 16-lane groups (two
+// v_permlane32_swap, two v_permlane16_swap) then hands every lane the eight
+// codes of its own MFMA slots for each K-step. Dequantisation stays in
+// registers: v_cvt_scalef32_pk_f32_fp4 (scale 1.0) turns two codes into two
+// fp32 values, a multiply by the E4M3 block scale (decoded by v_cvt_f32_fp8)
+// gives the exact weight, whose upper 16 bits are its bf16 pattern. Hidden
+// rows come through LDS as in the bf16 weight-streaming kernel, eight waves
+// per work-group held in lockstep by one LDS barrier per quad.
+// ---------------------------------------------------------------------------
+constexpr int NS_WAVES = 8;
+constexpr int NS_THREADS = 64 * NS_WAVES;
+constexpr int NS_KC = 128;          // K per quad == K per LDS chunk of hidden
+constexpr int NS_CPR = NS_KC / 8;   // 16-byte hidden pieces per row per chunk
+#ifndef LMHEAD_NS_P
+#define LMHEAD_NS_P 2
+#endif
+constexpr int NS_P = LMHEAD_NS_P;   // quads of weight loads in flight ahead of use
+
+constexpr int NS_SEGQ = 16;                 // quads per LDS segment of block scales
+constexpr int NS_SROW = NS_SEGQ + 1;        // 8-byte LDS words per weight row (1 word pad: banks)
+
+__device__ __forceinline__ int ns_hslot(int row, int ch) { return row * NS_CPR + (ch ^ (row & 15)); }
+
+// 4 x 4 transpose of 32-bit words across the four 16-lane rows of a wave:
+// on entry row g holds words D[g][0..3] in x0..x3; on exit x_t in row g
+// holds D[t][g].
+__device__ __forceinline__ void transpose4(uint32_t &x0, uint32_t &x1, uint32_t &x2, uint32_t &x3) {
+  auto a = __builtin_amdgcn_permlane32_swap(x0, x2, false, false);
+  auto b = __builtin_amdgcn_permlane32_swap(x1, x3, false, false);
+  auto c = __builtin_amdgcn_permlane16_swap(a[0], b[0], false, false);
+  auto d = __builtin_amdgcn_permlane16_swap(a[1], b[1], false, false);
+  x0 = c[0];
+  x1 = c[1];
+  x2 = d[0];
+  x3 = d[1];
+}
+
+// Eight codes (element 2p in the low nibble of byte p) times the block scale
+// -> eight exact bf16 weights in MFMA slot order.
+template <int P>
+__device__ __forceinline__ uint32_t dequant_pair(uint32_t codes, float s) {
+  const auto v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 1.0f, P);
+  const uint32_t lo = __builtin_bit_cast(uint32_t, v[0] * s);
+  const uint32_t hi = __builtin_bit_cast(uint32_t, v[1] * s);
+  return __builtin_amdgcn_perm(hi, lo, 0x07060302u);  // upper halves: (lo.bf16, hi.bf16)
+}
+
+__device__ __forceinline__ u32x4 dequant8_fast(uint32_t codes, float s) {
+  return u32x4{dequant_pair<0>(codes, s), dequant_pair<1>(codes, s), dequant_pair<2>(codes, s),
+               dequant_pair<3>(codes, s)};
+}
+
+template <int R, int NB>
+__global__ __launch_bounds__(NS_THREADS, 1) void nvfp4_stream_kernel(
+    const uint16_t *__restrict__ hidden, int64_t M, int64_t H, const uint8_t *__restrict__ codes,
+    const uint8_t *__restrict__ scales, int64_t V, float scale, const float *__restrict__ bias,
+    uint16_t *__restrict__ out) {
+  constexpr int ROWS = 16 * R;
+  constexpr int HPC = ROWS * NS_CPR;
+  constexpr int HL = (HPC + NS_THREADS - 1) / NS_THREADS;
+  // Weight prefetch depth in quads: with three or four row blocks a quad has
+  // enough MFMA work to cover the load latency with one quad in flight, and
+  // the registers go to the accumulators.
+  constexpr int P = R >= 3 ? 1 : NS_P;
+  constexpr int WROWS = NS_WAVES * NB * 16;              // weight rows of the work-group
+  constexpr int SPIECES = WROWS * NS_SEGQ;               // 8-byte scale pieces per segment
+  constexpr int SL = (SPIECES + NS_THREADS - 1) / NS_THREADS;
+  __shared__ u32x4 hs[2][HPC];
+  __shared__ u32x2 ss[WROWS * NS_SROW];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int li = lane & 15;
+  const int lg = lane >> 4;
+  const int64_t nmb = (M + 63) / 64;
+  const int64_t m0 = ((int64_t)blockIdx.x % nmb) * 64;
+  const int64_t cb0 = (((int64_t)blockIdx.x / nmb) * NS_WAVES + wave) * NB;
+  const bool active = cb0 * 16 < V;
+
+  const int64_t HC = H / 2, HS = H / 16;  // code and scale bytes per weight row
+  const int64_t wrows = V - cb0 * 16 < NB * 16 ? V - cb0 * 16 : NB * 16;
+  const int64_t base_row = active ? cb0 * 16 : 0;
+  const rsrc_t cr = make_rsrc(codes + base_row * HC, active ? (uint32_t)(wrows * HC) : 0u);
+  const uint32_t cvoff = (uint32_t)(li * HC + 16 * lg);
+  const uint32_t cjs = (uint32_t)(16 * HC);
+  // scale byte of K-step t of a quad for this lane group: 2t + lg/2
+  const uint32_t ssel = (lg >> 1) ? 0x07050301u : 0x06040200u;
+
+  // Block scales: the work-group's WROWS weight rows are contiguous in memory;
+  // each segment of NS_SEGQ quads (8 scale bytes per row per quad) is loaded
+  // cooperatively into LDS, so the scale stream is read once, in order.
+  const int64_t wg_row0 = ((int64_t)blockIdx.x / nmb) * WROWS;
+  const int64_t wg_rows = V - wg_row0 < WROWS ? V - wg_row0 : WROWS;
+  const rsrc_t sr = make_rsrc(scales + wg_row0 * HS, (uint32_t)(wg_rows * HS));
+  const int64_t nq = H / NS_KC;
+  // Scale piece i of this thread in segment `seg`: its load offset (pieces past
+  // the segment or the tile get an out-of-range offset and read zero) and its
+  // LDS word.
+  auto scale_off = [&](int i, int64_t seg) -> uint32_t {
+    const int64_t seg_quads = nq - seg * NS_SEGQ < NS_SEGQ ? nq - seg * NS_SEGQ : NS_SEGQ;
+    const int p = i * NS_THREADS + tid;
+    const int row = p / NS_SEGQ, e = p % NS_SEGQ;
+    return (i < SL && p < SPIECES && e < seg_quads)
+               ? (uint32_t)(row * HS + (seg * NS_SEGQ + e) * 8) : 0x80000000u;
+  };
+  auto scale_store = [&](int i, u32x2 v) {
+    const int p = i * NS_THREADS + tid;
+    if (i < SL && p < SPIECES) ss[(p / NS_SEGQ) * NS_SROW + p % NS_SEGQ] = v;
+  };
+  // Copies scale segment `seg` into LDS four pieces per thread at a time (few
+  // registers: it also runs inside the quad loop when H > 2048).
+  auto copy_scales = [&](int64_t seg) {
+#pragma unroll 1
+    for (int i0 = 0; i0 < SL; i0 += 4) {
+      u32x2 sreg[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        sreg[u] = __builtin_amdgcn_raw_buffer_load_b64(sr, scale_off(i0 + u, seg), 0, 0);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) scale_store(i0 + u, sreg[u]);
+    }
+  };
+  // LDS row of this lane's weight row in column block j
+  const int srow0 = (wave * NB * 16 + li) * NS_SROW;
+
+  const int64_t hrows = M - m0 < 64 ? M - m0 : 64;
+  const rsrc_t hr = make_rsrc(hidden + m0 * H, (uint32_t)(hrows * H * 2));
+  uint32_t hvoff[HL];
+  int hsl[HL];
+#pragma unroll
+  for (int i = 0; i < HL; ++i) {
+    const int idx = i * NS_THREADS + tid < HPC ? i * NS_THREADS + tid : HPC - 1;
+    const int row = idx / NS_CPR, ch = idx % NS_CPR;
+    hvoff[i] = (uint32_t)((row * H + 8 * ch) * 2);
+    hsl[i] = ns_hslot(row, ch);
+  }
+  u32x4 hreg[HL];
+  auto load_hidden = [&](int64_t q) {
+#pragma unroll
+    for (int i = 0; i < HL; ++i) hreg[i] = load16(hr, hvoff[i], (uint32_t)(q * NS_KC * 2));
+  };
+  auto store_hidden = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < HL; ++i) hs[buf][hsl[i]] = hreg[i];
+  };
+
+  u32x4 cq[P][NB];
+  auto load_q = [&](int slot, int64_t q) {
+#pragma unroll
+    for (int j = 0; j < NB; ++j) cq[slot][j] = load16(cr, cvoff, (uint32_t)(q * 64 + j * cjs));
+  };
+
+  f32x4 acc[NB][R];
+#pragma unroll
+  for (int j = 0; j < NB; ++j)
+#pragma unroll
+    for (int r = 0; r < R; ++r) acc[j][r] = zero4();
+
+  // One quad: transpose codes, pick scales, then four K-steps of the chain.
+  auto do_quad = [&](int slot, int64_t q) {
+    const int buf = (int)(q & 1);
+    if (q > 0 && q % NS_SEGQ == 0) {  // next scale segment (only when H > 2048)
+      lds_barrier();
+      copy_scales(q / NS_SEGQ);
+      lds_barrier();
+    }
+    uint32_t x[NB][4], sdw[NB];
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+      x[j][0] = cq[slot][j][0];
+      x[j][1] = cq[slot][j][1];
+      x[j][2] = cq[slot][j][2];
+      x[j][3] = cq[slot][j][3];
+      transpose4(x[j][0], x[j][1], x[j][2], x[j][3]);
+      const u32x2 sv = ss[srow0 + j * 16 * NS_SROW + (int)(q % NS_SEGQ)];
+      sdw[j] = __builtin_amdgcn_perm(sv[1], sv[0], ssel);
+    }
+    load_q(slot, q + P < nq ? q + P : nq - 1);
+    auto kstep_t = [&](auto tc) {
+      constexpr int t = decltype(tc)::value;
+      u32x4 a[R];
+#pragma unroll
+      for (int r = 0; r < R; ++r) a[r] = hs[buf][ns_hslot(16 * r + li, 4 * t + lg)];
+#pragma unroll
+      for (int j = 0; j < NB; ++j) {
+        const u32x4 b = dequant8_fast(x[j][t], __builtin_amdgcn_cvt_f32_fp8(sdw[j], t));
+#pragma unroll
+        for (int r = 0; r < R; ++r) acc[j][r] = kstep(acc[j][r], a[r], b);
+      }
+    };
+    kstep_t(std::integral_constant<int, 0>{});
+    kstep_t(std::integral_constant<int, 1>{});
+    kstep_t(std::integral_constant<int, 2>{});
+    kstep_t(std::integral_constant<int, 3>{});
+    sched_fence();
+    store_hidden(buf ^ 1);
+    lds_barrier();
+    load_hidden(q + 2 < nq ? q + 2 : nq - 1);
+  };
+
+  // Prologue: segment 0's scales into LDS, hidden chunk 0 into LDS, the first
+  // P code quads and hidden chunk 1 in flight.
+  copy_scales(0);
+  load_hidden(0);
+#pragma unroll
+  for (int p = 0; p < P; ++p) load_q(p, p < nq ? p : nq - 1);
+  store_hidden(0);
+  load_hidden(nq > 1 ? 1 : 0);
+  lds_barrier();
+
+  // ring slot of quad q is q % P: unroll P quads per iteration so every slot
+  // index is a compile-time constant
+  int64_t q = 0;
+  for (; q + P <= nq; q += P) {
+#pragma unroll
+    for (int p = 0; p < P; ++p) do_quad(p, q + p);
+  }
+#pragma unroll
+  for (int p = 0; p < P; ++p)
+    if (q + p < nq) do_quad(p, q + p);
+
+  if (!active) return;
+#pragma unroll
+  for (int j = 0; j < NB; ++j) {
+    const int64_t col = (cb0 + j) * 16 + li;
+    if (col >= V) continue;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+#pragma unroll
+      for (int qq = 0; qq < 4; ++qq) {
+        const int64_t row = m0 + 16 * r + 4 * lg + qq;
+        if (row < M) out[row * V + col] = bf16_rne(epilogue(acc[j][r][qq], scale, bias, col));
+      }
+    }
+  }
+}
+
+template <int R, int NB>
+int64_t ns_resident_slots() {
+  static std::atomic<int64_t> cached{0};
+  int64_t v = cached.load(std::memory_order_relaxed);
+  if (v == 0) {
+    int dev = 0, cus = 0, per_cu = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, nvfp4_stream_kernel<R, NB>,
+                                                     NS_THREADS, 0) != hipSuccess ||
+        cus <= 0 || per_cu <= 0)
+      return 256;
+    v = (int64_t)cus * per_cu;
+    cached.store(v, std::memory_order_relaxed);
+  }
+  return v;
+}
+
+template <int R, int NB>
+hipError_t launch_stream_nb(const Nvfp4Args &a, hipStream_t stream) {
+  const int64_t ncb = (a.V + 15) / 16;
+  const int64_t nvs = (ncb + NS_WAVES * NB - 1) / (NS_WAVES * NB);
+  dim3 grid((unsigned)(nvs * ((a.M + 63) / 64)));
+  hipLaunchKernelGGL((nvfp4_stream_kernel<R, NB>), grid, dim3(NS_THREADS), 0, stream, a.hidden,
+                     a.M, a.H, a.codes, a.scales, a.V, a.scale, a.bias, a.out);
+  return hipGetLastError();
+}
+
+template <int R>
+hipError_t launch_stream_r(const Nvfp4Args &a, hipStream_t stream) {
+  const int64_t ncb = (a.V + 15) / 16;
+  if ((ncb + 4 * NS_WAVES - 1) / (4 * NS_WAVES) <= ns_resident_slots<R, 4>())
+    return launch_stream_nb<R, 4>(a, stream);
+  return launch_stream_nb<R, 5>(a, stream);
 }
 
 }  // namespace
 
 hipError_t launch_nvfp4(const Nvfp4Args &a, hipStream_t stream) {
   const int64_t rows = a.M < 64 ? a.M : 64;
-  switch ((rows + 15) / 16) {
-    case 1: return launch_r<1>(a, stream);
-    case 2: return launch_r<2>(a, stream);
-    case 3: return launch_r<3>(a, stream);
-    default: return launch_r<4>(a, stream);
+  const int rb = (int)((rows + 15) / 16);
+  // the streaming kernel reads 8 scale bytes at a time: rows of 8k bytes on an
+  // 8-byte aligned base
+  if (a.H % NS_KC == 0 && reinterpret_cast<uintptr_t>(a.scales) % 8 == 0) {
+    switch (rb) {
+      case 1: return launch_stream_r<1>(a, stream);
+      case 2: return launch_stream_r<2>(a, stream);
+      case 3: return launch_stream_r<3>(a, stream);
+      default: return launch_stream_r<4>(a, stream);
+    }
+  }
+  switch (rb) {  // any H % 32 == 0: per-K-step byte loads, same K-step chain
+    case 1: return launch_generic_r<1>(a, stream);
+    case 2: return launch_generic_r<2>(a, stream);
+    case 3: return launch_generic_r<3>(a, stream);
+    default: return launch_generic_r<4>(a, stream);
   }
 }
 

@@ -1,16 +1,30 @@
 // skinny.hip -- the weight-streaming split-V kernel for decode-sized M (<= 64).
 //
-// At decode sizes the projection is a stream of the whole bf16 weight from
-// HBM (the sglang digest's motivation section: the fp32 head's cost was the
-// weight traffic, which the bf16 x bf16 -> fp32 path cuts to one read of the
-// bf16 weight). Each wave owns NB column blocks of 16 vocabulary rows and
-// walks the full H for them, loading 16 contiguous bytes per lane per weight
-// row straight into the MFMA B operand; the hidden rows (<= 64, L2-resident)
-// feed the A operand the same way. The K-step chain is the one of kstep.hpp,
-// so the results equal the tiled GEMM's bit for bit.
+// At decode sizes the projection is one stream of the whole bf16 weight from
+// HBM (the sglang digest's motivation section: the fp32 head's cost was weight
+// traffic, which the bf16 x bf16 -> fp32 path cuts to one read of the bf16
+// weight). Each wave owns NB column blocks of 16 vocabulary rows and walks the
+// full H for them: every lane loads 16 contiguous bytes of one weight row per
+// K-step straight into the MFMA B operand, P K-steps ahead of their use. The
+// hidden rows (<= 64) are staged through LDS in KC-element K chunks,
+// double-buffered, so the waves of a work-group read them from L2 once. The
+// K-step chain is the one of kstep.hpp, so the results equal the tiled GEMM's
+// bit for bit.
 //
-// Grid (1-D): vocabulary slices of 4 waves * NB * 16 columns times 64-row
-// blocks of M (one block for M <= 64; the forced-path test drives more).
+// Measured on MI355X (HBM read of the 1.05 GB decode weight): the order in
+// which the GPU as a whole walks the weight decides the bandwidth. Waves that
+// drift apart in K reach ~4.8 TB/s; eight waves per work-group held in
+// lockstep by the per-chunk LDS barrier (512 consecutive weight rows at the
+// same K) reach ~5.8 TB/s. The barrier is an LDS-only barrier so prefetched
+// weight loads stay in flight across it.
+//
+// Launch: the host picks NB so that every wave of the grid is resident at
+// once (a second, partial round of waves would stream at a fraction of the
+// bandwidth). Grid (1-D): vocabulary slices of WAVES * NB column blocks,
+// times 64-row blocks of M (one for M <= 64; the forced-path test drives
+// more).
+#include <atomic>
+
 #include "kstep.hpp"
 #include "launch.hpp"
 
@@ -18,66 +32,160 @@ namespace lmhead {
 
 namespace {
 
-constexpr int SK_WAVES = 4;
-constexpr int SK_NB = 4;  // 16-column blocks per wave
+#ifndef LMHEAD_SK_WAVES
+#define LMHEAD_SK_WAVES 8
+#endif
+#ifndef LMHEAD_SK_KC
+#define LMHEAD_SK_KC 128
+#endif
+constexpr int SK_WAVES = LMHEAD_SK_WAVES;
+constexpr int SK_THREADS = 64 * SK_WAVES;
+constexpr int SK_KC = LMHEAD_SK_KC;     // K elements per LDS chunk of hidden (one barrier each)
+constexpr int SK_SPC = SK_KC / KSTEP;   // K-steps per chunk
+constexpr int SK_CPR = SK_KC / 8;       // 16-byte pieces per hidden row per chunk
+#ifndef LMHEAD_SK_P
+#define LMHEAD_SK_P 4
+#endif
+#ifndef LMHEAD_SK_POLICY
+#define LMHEAD_SK_POLICY LOAD_DEFAULT
+#endif
+constexpr int SK_P = LMHEAD_SK_P;       // weight prefetch depth, in K-steps (divides SK_SPC)
+// Cache policy of the weight stream. Measured on MI355X: the non-temporal
+// hint makes this access pattern about 1.5x slower, so the default policy.
+constexpr int SK_POLICY = LMHEAD_SK_POLICY;
 
-template <int R, typename OutT>
-__global__ __launch_bounds__(256) void skinny_kernel(const uint16_t *__restrict__ hidden, int64_t M,
-                                                     int64_t H, const uint16_t *__restrict__ W,
-                                                     int64_t V, float alpha,
-                                                     const float *__restrict__ bias,
-                                                     OutT *__restrict__ out) {
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+// LDS slot of 16-byte piece `ch` of hidden row `row` (xor swizzle: the 16
+// rows one K-step reads land in different banks).
+__device__ __forceinline__ int hslot(int row, int ch) {
+  return row * SK_CPR + (ch ^ (row & (SK_CPR < 16 ? SK_CPR - 1 : 15)));
+}
+
+template <int R, int NB, typename OutT>
+__global__ __launch_bounds__(SK_THREADS, SK_WAVES >= 8 ? 1 : 2) void skinny_kernel(
+    const uint16_t *__restrict__ hidden, int64_t M, int64_t H, const uint16_t *__restrict__ W,
+    int64_t V, float alpha, const float *__restrict__ bias, OutT *__restrict__ out) {
+  constexpr int ROWS = 16 * R;
+  constexpr int HPC = ROWS * SK_CPR;                           // hidden pieces per chunk
+  constexpr int HL = (HPC + SK_THREADS - 1) / SK_THREADS;      // ... per thread
+  __shared__ u32x4 hs[2][ROWS * SK_CPR];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: resources stay scalar
   const int li = lane & 15;
   const int lg = lane >> 4;
-  // 1-D grid: the 64-row blocks of one vocabulary slice are neighbours.
   const int64_t nmb = (M + 63) / 64;
   const int64_t m0 = ((int64_t)blockIdx.x % nmb) * 64;
-  const int64_t col0 = (((int64_t)blockIdx.x / nmb) * SK_WAVES + wave) * (SK_NB * 16);
-  if (col0 >= V) return;  // no barriers in this kernel: a wave may leave early
+  const int64_t cb0 = (((int64_t)blockIdx.x / nmb) * SK_WAVES + wave) * NB;  // first column block
+  const bool active = cb0 * 16 < V;  // wave-uniform
 
-  const u32x4 *bp[SK_NB];
-  bool bv[SK_NB];
+  // Weight: one buffer resource per wave over its NB * 16 rows (rows past V
+  // read as zero); lane offset li*H + 8*lg elements, column block j at
+  // j*16*H elements (a scalar offset), K-step s at 32*s elements.
+  const int64_t wrows = V - cb0 * 16 < NB * 16 ? V - cb0 * 16 : NB * 16;
+  const rsrc_t wr = make_rsrc(W + (active ? cb0 * 16 : 0) * H,
+                              active ? (uint32_t)(wrows * H * 2) : 0u);
+  const uint32_t wvoff = (uint32_t)((li * H + 8 * lg) * 2);
+  const uint32_t wjstride = (uint32_t)(16 * H * 2);
+
+  // Hidden: one resource over the work-group's <= 64 rows (rows past M read
+  // as zero); this thread stages pieces (row, 16-byte piece) of each chunk.
+  const int64_t hrows = M - m0 < 64 ? M - m0 : 64;
+  const rsrc_t hr = make_rsrc(hidden + m0 * H, (uint32_t)(hrows * H * 2));
+  uint32_t hvoff[HL];
+  int hsl[HL], hch[HL];
 #pragma unroll
-  for (int j = 0; j < SK_NB; ++j) {
-    int64_t col = col0 + 16 * j + li;
-    bv[j] = col < V;
-    bp[j] = reinterpret_cast<const u32x4 *>(W + (bv[j] ? col : 0) * H + 8 * lg);
-  }
-  const u32x4 *ap[R];
-  bool av[R];
-#pragma unroll
-  for (int r = 0; r < R; ++r) {
-    int64_t row = m0 + 16 * r + li;
-    av[r] = row < M;
-    ap[r] = reinterpret_cast<const u32x4 *>(hidden + (av[r] ? row : 0) * H + 8 * lg);
+  for (int i = 0; i < HL; ++i) {
+    // threads past the chunk's last piece re-stage the last piece (same bytes, same slot)
+    const int idx = i * SK_THREADS + tid < HPC ? i * SK_THREADS + tid : HPC - 1;
+    const int row = idx / SK_CPR, ch = idx % SK_CPR;
+    hvoff[i] = (uint32_t)((row * H + 8 * ch) * 2);
+    hsl[i] = hslot(row, ch);
+    hch[i] = ch;
   }
 
-  f32x4 acc[SK_NB][R];
+  const int64_t nk = H / KSTEP;
+  const int64_t hpieces = H / 8;
+  const int64_t nchunks = (nk + SK_SPC - 1) / SK_SPC;
+
+  u32x4 hreg[HL];
+  auto load_hidden = [&](int64_t c) {
+    const uint32_t soff = (uint32_t)(c * SK_KC * 2);
 #pragma unroll
-  for (int j = 0; j < SK_NB; ++j)
+    for (int i = 0; i < HL; ++i) {
+      // a piece past the row end (H % 256 != 0) gets an offset past the
+      // resource (2^31 + soff cannot wrap), which reads zero without a branch
+      const uint32_t v = (c * SK_CPR + hch[i] < hpieces) ? hvoff[i] : 0x80000000u;
+      hreg[i] = load16(hr, v, soff);
+    }
+  };
+  auto store_hidden = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < HL; ++i) hs[buf][hsl[i]] = hreg[i];
+  };
+
+  u32x4 wb[SK_P][NB];
+  auto load_w = [&](int slot, int64_t step) {
+    const uint32_t soff = (uint32_t)(step * KSTEP * 2);
+#pragma unroll
+    for (int j = 0; j < NB; ++j) wb[slot][j] = load16<SK_POLICY>(wr, wvoff, soff + j * wjstride);
+  };
+
+  f32x4 acc[NB][R];
+#pragma unroll
+  for (int j = 0; j < NB; ++j)
 #pragma unroll
     for (int r = 0; r < R; ++r) acc[j][r] = zero4();
 
-  const u32x4 z = {0u, 0u, 0u, 0u};
-  const int64_t nk = H / KSTEP;
-#pragma unroll 4
-  for (int64_t s = 0; s < nk; ++s) {
-    u32x4 b[SK_NB], a[R];
+  // One K-step of the chain on LDS buffer `buf`, slot `slot` of the weight
+  // ring; then the ring slot is refilled P steps ahead (clamped to the last
+  // step: the refetch of an already-read piece costs a cache hit, not a branch).
+  auto kstep_all = [&](int buf, int s, int slot, int64_t step) {
+    u32x4 a[R];
 #pragma unroll
-    for (int j = 0; j < SK_NB; ++j) b[j] = bv[j] ? bp[j][s * 4] : z;
+    for (int r = 0; r < R; ++r) a[r] = hs[buf][hslot(16 * r + li, 4 * s + lg)];
 #pragma unroll
-    for (int r = 0; r < R; ++r) a[r] = av[r] ? ap[r][s * 4] : z;
+    for (int j = 0; j < NB; ++j)
 #pragma unroll
-    for (int j = 0; j < SK_NB; ++j)
+      for (int r = 0; r < R; ++r) acc[j][r] = kstep(acc[j][r], a[r], wb[slot][j]);
+    const int64_t next = step + SK_P < nk ? step + SK_P : nk - 1;
+    load_w(slot, next);
+  };
+
+  // prologue: hidden chunk 0 in LDS, the first P weight K-steps in flight,
+  // hidden chunk 1 in flight. Waves past the vocabulary end run the same
+  // code on zero-filled loads (their resource is empty) and store nothing.
+  load_hidden(0);
 #pragma unroll
-      for (int r = 0; r < R; ++r) acc[j][r] = kstep(acc[j][r], a[r], b[j]);
+  for (int p = 0; p < SK_P; ++p) load_w(p, p < nk ? p : nk - 1);
+  store_hidden(0);  // waits for hidden chunk 0 only: loads complete in issue order
+  load_hidden(nchunks > 1 ? 1 : 0);
+  lds_barrier();
+
+  // Full chunks: straight-line code with no branches around the loads, so
+  // the waits before each MFMA count exactly the loads still in flight.
+  const int64_t nfull = nk / SK_SPC;
+  for (int64_t c = 0; c < nfull; ++c) {
+    const int buf = (int)(c & 1);
+#pragma unroll
+    for (int s = 0; s < SK_SPC; ++s) kstep_all(buf, s, s % SK_P, c * SK_SPC + s);
+    sched_fence();
+    store_hidden(buf ^ 1);
+    lds_barrier();
+    load_hidden(c + 2 < nchunks ? c + 2 : nchunks - 1);
+  }
+  // Partial last chunk (H % 256 != 0).
+  if (nfull < nchunks) {
+    const int buf = (int)(nfull & 1);
+#pragma unroll
+    for (int s = 0; s < SK_SPC; ++s)
+      if (nfull * SK_SPC + s < nk) kstep_all(buf, s, s % SK_P, nfull * SK_SPC + s);
   }
 
+  if (!active) return;
 #pragma unroll
-  for (int j = 0; j < SK_NB; ++j) {
-    const int64_t col = col0 + 16 * j + li;
+  for (int j = 0; j < NB; ++j) {
+    const int64_t col = (cb0 + j) * 16 + li;
     if (col >= V) continue;
 #pragma unroll
     for (int r = 0; r < R; ++r) {
@@ -90,31 +198,63 @@ __global__ __launch_bounds__(256) void skinny_kernel(const uint16_t *__restrict_
   }
 }
 
-template <int R>
-hipError_t launch_r(const Bf16Args &a, hipStream_t stream) {
-  dim3 grid((unsigned)(((a.V + SK_WAVES * SK_NB * 16 - 1) / (SK_WAVES * SK_NB * 16)) *
-                       ((a.M + 63) / 64)));
-  dim3 block(64 * SK_WAVES);
-  if (a.out_bf16)
-    hipLaunchKernelGGL((skinny_kernel<R, uint16_t>), grid, block, 0, stream, a.hidden, a.M, a.H,
-                       a.W, a.V, a.alpha, a.bias, static_cast<uint16_t *>(a.out));
-  else
-    hipLaunchKernelGGL((skinny_kernel<R, float>), grid, block, 0, stream, a.hidden, a.M, a.H, a.W,
-                       a.V, a.alpha, a.bias, static_cast<float *>(a.out));
+// Work-groups of one kernel variant resident on the device at once, queried
+// once per variant (the library's only cached state; every GPU it runs on is
+// taken to be the same model).
+template <int R, int NB, typename OutT>
+int64_t resident_slots() {
+  static std::atomic<int64_t> cached{0};
+  int64_t v = cached.load(std::memory_order_relaxed);
+  if (v == 0) {
+    int dev = 0, cus = 0, per_cu = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, skinny_kernel<R, NB, OutT>,
+                                                     SK_THREADS, 0) != hipSuccess ||
+        cus <= 0 || per_cu <= 0)
+      return 256;  // conservative: one work-group per CU of a 256-CU part
+    v = (int64_t)cus * per_cu;
+    cached.store(v, std::memory_order_relaxed);
+  }
+  return v;
+}
+
+template <int R, int NB, typename OutT>
+hipError_t launch_nb(const Bf16Args &a, hipStream_t stream) {
+  const int64_t ncb = (a.V + 15) / 16;
+  const int64_t nvs = (ncb + SK_WAVES * NB - 1) / (SK_WAVES * NB);
+  dim3 grid((unsigned)(nvs * ((a.M + 63) / 64)));
+  hipLaunchKernelGGL((skinny_kernel<R, NB, OutT>), grid, dim3(SK_THREADS), 0, stream, a.hidden,
+                     a.M, a.H, a.W, a.V, a.alpha, a.bias, static_cast<OutT *>(a.out));
   return hipGetLastError();
+}
+
+// NB = 4 (more, smaller waves) when that grid is resident in one round, else
+// NB = 5 (one round up to V = 163840 at two work-groups per CU).
+template <int R, typename OutT>
+hipError_t launch_r(const Bf16Args &a, hipStream_t stream) {
+  const int64_t ncb = (a.V + 15) / 16;
+  if ((ncb + 4 * SK_WAVES - 1) / (4 * SK_WAVES) <= resident_slots<R, 4, OutT>())
+    return launch_nb<R, 4, OutT>(a, stream);
+  return launch_nb<R, 5, OutT>(a, stream);
+}
+
+template <typename OutT>
+hipError_t launch_t(const Bf16Args &a, hipStream_t stream) {
+  // Row blocks per 64-row chunk: only as many as the rows present need.
+  const int64_t rows = a.M < 64 ? a.M : 64;
+  switch ((rows + 15) / 16) {
+    case 1: return launch_r<1, OutT>(a, stream);
+    case 2: return launch_r<2, OutT>(a, stream);
+    case 3: return launch_r<3, OutT>(a, stream);
+    default: return launch_r<4, OutT>(a, stream);
+  }
 }
 
 }  // namespace
 
 hipError_t launch_skinny(const Bf16Args &a, hipStream_t stream) {
-  // Row blocks per 64-row chunk: only as many as the rows present need.
-  const int64_t rows = a.M < 64 ? a.M : 64;
-  switch ((rows + 15) / 16) {
-    case 1: return launch_r<1>(a, stream);
-    case 2: return launch_r<2>(a, stream);
-    case 3: return launch_r<3>(a, stream);
-    default: return launch_r<4>(a, stream);
-  }
+  return a.out_bf16 ? launch_t<uint16_t>(a, stream) : launch_t<float>(a, stream);
 }
 
 }  // namespace lmhead
