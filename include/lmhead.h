@@ -78,12 +78,15 @@ typedef enum {
 /* Shape contract (both entry points):
  *   M >= 0, H >= 32 and H % 32 == 0, V >= 1,
  *   M <= LMHEAD_MAX_M, H <= LMHEAD_MAX_H, V <= LMHEAD_MAX_V.
+ * (The kernels address one work-group's block of output rows, and one wave's
+ * slice of weight rows, with 32-bit byte offsets; the maxima keep every such
+ * block below 1 GiB. V <= 2^20 covers every vocabulary in use.)
  * Alignment: hidden, W, w_e2m1 and out 16-byte aligned; bias 4-byte aligned;
  * w_scale 2-byte aligned. (torch allocations are 256-byte aligned; a row
  * sub-range W + v0*H stays 16-byte aligned because H % 32 == 0.) */
 #define LMHEAD_MAX_M ((int64_t)1 << 24)
 #define LMHEAD_MAX_H ((int64_t)1 << 16)
-#define LMHEAD_MAX_V ((int64_t)1 << 30)
+#define LMHEAD_MAX_V ((int64_t)1 << 20)
 
 /* The projection with a bf16 weight.
  *   hidden    bf16 [M, H]                       (device, read)

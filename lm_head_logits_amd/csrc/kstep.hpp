@@ -122,17 +122,68 @@ __device__ __forceinline__ uint16_t bf16_rne(float f) {
   return (uint16_t)(u >> 16);
 }
 
+// The epilogue with the bias value already loaded (has_bias false: no add).
+__device__ __forceinline__ float epilogue_v(float acc, float alpha, bool has_bias, float b) {
+  float t = __fmul_rn(alpha, acc);
+  if (has_bias) t = __fadd_rn(t, b);
+  return t;
+}
+
+// One output element through a buffer resource: fp32, or bf16 rounded to
+// nearest even. Offsets past the resource are dropped by the hardware.
 template <typename OutT>
-__device__ __forceinline__ void store_out(OutT *out, int64_t idx, float t);
+__device__ __forceinline__ void store_c(rsrc_t r, uint32_t voff, uint32_t soff, float t);
 
 template <>
-__device__ __forceinline__ void store_out<float>(float *out, int64_t idx, float t) {
-  out[idx] = t;
+__device__ __forceinline__ void store_c<float>(rsrc_t r, uint32_t voff, uint32_t soff, float t) {
+  __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, t), r, voff, soff, 0);
 }
 
 template <>
-__device__ __forceinline__ void store_out<uint16_t>(uint16_t *out, int64_t idx, float t) {
-  out[idx] = bf16_rne(t);
+__device__ __forceinline__ void store_c<uint16_t>(rsrc_t r, uint32_t voff, uint32_t soff, float t) {
+  __builtin_amdgcn_raw_buffer_store_b16(bf16_rne(t), r, voff, soff, 0);
+}
+
+// An offset past any output resource (resources are < 1 GiB and scalar
+// offsets < 1 GiB, so the sum cannot wrap into range): the store is dropped.
+constexpr uint32_t OFF_NONE = 0x80000000u;
+
+// Epilogue of one wave's output blocks, shared by every kernel.
+//   acc(i, j)   accumulator of 16-row block i, 16-column block j
+//   rows        output rows of the block (from the wave's first row), <= 16*FM
+//   rbase       row of the wave's first output row; cbase: its first column
+// Output element (rbase + 16 i + 4 lg + q, cbase + 16 j + li) of a row-major
+// [M, V] matrix. Rows past `rows` are dropped by the resource bound, columns
+// >= V by an out-of-range offset; the bias is read once per column.
+template <int FM, int FN, typename OutT, typename Acc>
+__device__ __forceinline__ void store_blocks(Acc &&acc, OutT *out, int64_t rbase, int64_t rows,
+                                             int64_t cbase, int64_t V, float alpha,
+                                             const float *__restrict__ bias) {
+  const int lane = threadIdx.x & 63;
+  const int li = lane & 15, lg = lane >> 4;
+  // Based at the wave's first element; its size runs to the end of the last
+  // row the wave owns, so no store of a valid (row, column) is dropped. A wave
+  // with no valid row or whose first column is past V gets an empty resource
+  // (a negative size would wrap to a huge one and let the out-of-range column
+  // offset below land inside it).
+  const bool any = rows > 0 && cbase < V;
+  const rsrc_t r = make_rsrc(any ? out + rbase * V + cbase : out,
+                             any ? (uint32_t)(((rows - 1) * V + (V - cbase)) * sizeof(OutT)) : 0u);
+  const uint32_t lvoff = (uint32_t)((4 * lg * V + li) * sizeof(OutT));
+  const bool has_bias = bias != nullptr;
+#pragma unroll
+  for (int j = 0; j < FN; ++j) {
+    const int64_t col = cbase + 16 * j + li;
+    const bool ok = col < V;
+    const float b = (has_bias && ok) ? bias[col] : 0.0f;
+    const uint32_t voff = ok ? lvoff + (uint32_t)(16 * j * sizeof(OutT)) : OFF_NONE;
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        store_c<OutT>(r, voff, (uint32_t)((16 * i + q) * V * sizeof(OutT)),
+                      epilogue_v(acc(i, j)[q], alpha, has_bias, b));
+  }
 }
 
 }  // namespace lmhead

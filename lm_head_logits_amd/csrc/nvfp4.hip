@@ -387,19 +387,8 @@ __global__ __launch_bounds__(NS_THREADS, 1) void nvfp4_stream_kernel(
     if (q + p < nq) do_quad(p, q + p);
 
   if (!active) return;
-#pragma unroll
-  for (int j = 0; j < NB; ++j) {
-    const int64_t col = (cb0 + j) * 16 + li;
-    if (col >= V) continue;
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-#pragma unroll
-      for (int qq = 0; qq < 4; ++qq) {
-        const int64_t row = m0 + 16 * r + 4 * lg + qq;
-        if (row < M) out[row * V + col] = bf16_rne(epilogue(acc[j][r][qq], scale, bias, col));
-      }
-    }
-  }
+  store_blocks<R, NB>([&](int i, int j) -> f32x4 & { return acc[j][i]; }, out, m0,
+                      M - m0 < 16 * R ? M - m0 : 16 * R, cb0 * 16, V, scale, bias);
 }
 
 template <int R, int NB>

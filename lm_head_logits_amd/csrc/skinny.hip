@@ -183,19 +183,9 @@ __global__ __launch_bounds__(SK_THREADS, SK_WAVES >= 8 ? 1 : 2) void skinny_kern
   }
 
   if (!active) return;
-#pragma unroll
-  for (int j = 0; j < NB; ++j) {
-    const int64_t col = (cb0 + j) * 16 + li;
-    if (col >= V) continue;
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int64_t row = m0 + 16 * r + 4 * lg + q;
-        if (row < M) store_out<OutT>(out, row * V + col, epilogue(acc[j][r][q], alpha, bias, col));
-      }
-    }
-  }
+  // acc is indexed [column block][row block]
+  store_blocks<R, NB>([&](int i, int j) -> f32x4 & { return acc[j][i]; }, out, m0,
+                      M - m0 < 16 * R ? M - m0 : 16 * R, cb0 * 16, V, alpha, bias);
 }
 
 // Work-groups of one kernel variant resident on the device at once, queried

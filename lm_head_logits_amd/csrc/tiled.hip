@@ -1,19 +1,32 @@
 // tiled.hip -- LDS-tiled MFMA GEMM for large M (verify and prefill).
 //
 // logits[M, V] = alpha * hidden[M, H] . W[V, H]^T (+ bias) with bf16 inputs,
-// fp32 accumulation and fp32 or bf16 output, the fast path of the sglang
+// fp32 accumulation and fp32 or bf16 output: the fast path of the sglang
 // digest (key source excerpt of _compute_lm_head: a bf16 x bf16 -> fp32 mm
-// with no fp32 copies of either operand) and the fused alpha of vLLM PR 49120
-// (section "muP is folded into the fp32 GEMM").
+// with no fp32 copy of either operand) with the alpha of vLLM PR 49120
+// folded into the epilogue (section "muP is folded into the fp32 GEMM").
 //
-// Work-group tile BM x BN, K staged through LDS BK at a time; four waves in a
-// 2 x 2 arrangement, each owning a (BM/2) x (BN/2) sub-tile of 16 x 16 MFMA
-// blocks. Every output element is built by the K-step chain of kstep.hpp --
-// ascending K, one accumulator, the same operand map -- so a row's bits equal
-// the skinny kernel's and do not depend on M.
+// Work-group tile TM x 256 output elements with eight waves: TM = 256 in a
+// 4 x 2 arrangement (64 x 128 per wave), or TM = 128 (when that covers M) in
+// 2 x 4 (64 x 64 per wave). Each wave's 16 x 16 MFMA blocks keep their fp32
+// accumulators in registers for the whole K loop. K is staged through LDS 64 elements at a time, double-buffered:
+// the loads of stage k+1 are issued as direct-to-LDS buffer loads
+// (buffer_load_dwordx4 ... lds, no registers) before the MFMAs of stage k run,
+// and one barrier per stage hands the buffers over. Every output element is
+// built by the K-step chain of kstep.hpp -- ascending K, one accumulator, the
+// same operand map -- so a row's bits equal the weight-streaming kernel's and
+// do not depend on M.
 //
-// LDS layout: [row][16-byte chunk] with the chunk index xor-ed by (row & 7),
-// so the 16 rows a K-step reads spread over the banks.
+// LDS layout of a stage: [row][8 pieces of 16 bytes]; piece c of row r sits in
+// slot c ^ ((r >> 1) & 7), so the 16 rows one MFMA operand read touches land
+// on 16 distinct 4-bank groups (conflict-free ds_read_b128). The direct loads
+// write 64 consecutive slots per instruction; the swizzle is applied on the
+// global side by choosing which piece each lane fetches.
+//
+// Tile order: work-groups are dispatched to the eight XCDs round-robin, so
+// block b is remapped to tile t such that consecutive tiles run on one XCD;
+// tiles are numbered M-fastest, so the work-groups sharing a weight tile share
+// that XCD's L2 and the weight is read from HBM about once.
 #include "kstep.hpp"
 #include "launch.hpp"
 
@@ -21,153 +34,175 @@ namespace lmhead {
 
 namespace {
 
-constexpr int TL_BM = 128;
-constexpr int TL_BN = 128;
-constexpr int TL_BK = 64;                 // two K-steps per LDS stage
-constexpr int TL_CH = TL_BK / 8;          // 16-byte chunks per row per stage
-constexpr int TL_THREADS = 256;
-constexpr int TL_WM = TL_BM / 2;          // rows per wave
-constexpr int TL_WN = TL_BN / 2;          // columns per wave
-constexpr int TL_FM = TL_WM / 16;         // 16-row blocks per wave
-constexpr int TL_FN = TL_WN / 16;         // 16-column blocks per wave
-constexpr int TL_LOADS_A = TL_BM * TL_CH / TL_THREADS;
-constexpr int TL_LOADS_B = TL_BN * TL_CH / TL_THREADS;
+constexpr int TL_TN = 256;
+constexpr int TL_TK = 64;                 // two K-steps per LDS stage
+constexpr int TL_PPR = TL_TK / 8;         // 16-byte pieces per row per stage
+constexpr int TL_XCDS = 8;
 
-__device__ __forceinline__ int swz(int row, int chunk) { return row * TL_CH + (chunk ^ (row & 7)); }
+__device__ __forceinline__ int tl_slot(int row, int piece) {
+  return row * TL_PPR + (piece ^ ((row >> 1) & 7));
+}
 
-template <typename OutT>
-__global__ __launch_bounds__(TL_THREADS) void tiled_kernel(const uint16_t *__restrict__ hidden,
-                                                           int64_t M, int64_t H,
-                                                           const uint16_t *__restrict__ W,
-                                                           int64_t V, float alpha,
-                                                           const float *__restrict__ bias,
-                                                           OutT *__restrict__ out) {
-  __shared__ u32x4 As[TL_BM * TL_CH];
-  __shared__ u32x4 Bs[TL_BN * TL_CH];
+typedef __attribute__((address_space(3))) void lds_void;
+
+// One direct-to-LDS load: 64 lanes x 16 bytes into 1 KB of LDS at `dst`
+// (wave-uniform), lane l landing at dst + 16 l.
+__device__ __forceinline__ void dma16(rsrc_t r, void *dst, uint32_t voff, uint32_t soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)dst, 16, voff, soff, 0, 0);
+}
+
+// WM x WN waves; each owns a (TM / WM) x (TN / WN) sub-tile of at most 4 x 8
+// MFMA blocks: <= 128 fp32 accumulators per lane, which the compiler keeps in
+// ordinary VGPRs next to the operand fragments (two waves per SIMD).
+template <int TM, int WM, int WN, typename OutT>
+__global__ __launch_bounds__(64 * WM * WN, 1) void tiled_kernel(const uint16_t *__restrict__ hidden,
+                                                               int64_t M, int64_t H,
+                                                               const uint16_t *__restrict__ W,
+                                                               int64_t V, float alpha,
+                                                               const float *__restrict__ bias,
+                                                               OutT *__restrict__ out) {
+  constexpr int NW = WM * WN;
+  constexpr int SM = TM / WM, SN = TL_TN / WN;   // wave sub-tile
+  constexpr int FM = SM / 16;                    // 16-row blocks per wave
+  constexpr int FN = SN / 16;                    // 16-column blocks per wave
+  constexpr int A_DMA = TM * TL_PPR / 64 / NW;     // direct loads per wave per stage (A)
+  constexpr int B_DMA = TL_TN * TL_PPR / 64 / NW;  // (B)
+  static_assert(A_DMA * 64 * NW == TM * TL_PPR && B_DMA * 64 * NW == TL_TN * TL_PPR, "tiling");
+  // Two separately declared buffers per operand (not one array indexed by a
+  // variable), so the compiler can tell the stage being loaded from the stage
+  // being read and does not wait for the former before reading the latter.
+  __shared__ u32x4 As0[TM * TL_PPR], As1[TM * TL_PPR];
+  __shared__ u32x4 Bs0[TL_TN * TL_PPR], Bs1[TL_TN * TL_PPR];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int li = lane & 15;
   const int lg = lane >> 4;
-  const int wm = wave >> 1;
-  const int wn = wave & 1;
-  // 1-D grid: the M tiles of one weight tile are neighbours in launch order.
-  const int64_t nmt = (M + TL_BM - 1) / TL_BM;
-  const int64_t m0 = ((int64_t)blockIdx.x % nmt) * TL_BM;
-  const int64_t n0 = ((int64_t)blockIdx.x / nmt) * TL_BN;
+  const int wm = wave / WN;
+  const int wn = wave % WN;
 
-  // Global -> register staging: each thread moves TL_LOADS_{A,B} 16-byte chunks.
-  const u32x4 *ga[TL_LOADS_A];
-  bool va[TL_LOADS_A];
-  int la[TL_LOADS_A], ca[TL_LOADS_A];
-#pragma unroll
-  for (int p = 0; p < TL_LOADS_A; ++p) {
-    int idx = p * TL_THREADS + tid;
-    int row = idx / TL_CH, ch = idx % TL_CH;
-    int64_t grow = m0 + row;
-    va[p] = grow < M;
-    ga[p] = reinterpret_cast<const u32x4 *>(hidden + (va[p] ? grow : 0) * H) + ch;
-    la[p] = swz(row, ch);
-    ca[p] = ch;
-  }
-  const u32x4 *gb[TL_LOADS_B];
-  bool vb[TL_LOADS_B];
-  int lb[TL_LOADS_B], cb[TL_LOADS_B];
-#pragma unroll
-  for (int p = 0; p < TL_LOADS_B; ++p) {
-    int idx = p * TL_THREADS + tid;
-    int row = idx / TL_CH, ch = idx % TL_CH;
-    int64_t gcol = n0 + row;
-    vb[p] = gcol < V;
-    gb[p] = reinterpret_cast<const u32x4 *>(W + (vb[p] ? gcol : 0) * H) + ch;
-    lb[p] = swz(row, ch);
-    cb[p] = ch;
-  }
+  // XCD-aware tile index, M-tiles fastest.
+  const int64_t nmt = (M + TM - 1) / TM;
+  const int64_t ntiles = nmt * ((V + TL_TN - 1) / TL_TN);
+  const int64_t b = blockIdx.x;
+  const int64_t q = ntiles / TL_XCDS, r = ntiles % TL_XCDS;
+  const int64_t xcd = b % TL_XCDS, pos = b / TL_XCDS;
+  const int64_t t = xcd < r ? xcd * (q + 1) + pos : r * (q + 1) + (xcd - r) * q + pos;
+  const int64_t m0 = (t % nmt) * TM;
+  const int64_t n0 = (t / nmt) * TL_TN;
 
-  const u32x4 z = {0u, 0u, 0u, 0u};
-  u32x4 ra[TL_LOADS_A], rb[TL_LOADS_B];
-  // A stage covers k in [kt*BK, kt*BK + BK); its second half lies past the
-  // row end when H / 32 is odd, and those chunks are never read from memory.
-  const int64_t hch = H / 8;  // 16-byte chunks per row
-  auto load_stage = [&](int64_t kt) {
-    const int64_t off = kt * TL_CH;  // in 16-byte chunks
+  const int64_t arows = M - m0 < TM ? M - m0 : TM;
+  const int64_t brows = V - n0 < TL_TN ? V - n0 : TL_TN;
+  const rsrc_t ar = make_rsrc(hidden + m0 * H, (uint32_t)(arows * H * 2));
+  const rsrc_t br = make_rsrc(W + n0 * H, (uint32_t)(brows * H * 2));
+
+  // Direct-load plan: instruction u of this wave fills LDS bytes
+  // [1 KB * (wave * N + u), ...): 8 rows x 8 slots; lane l -> slot l % 8 of
+  // row 8 * (wave * N + u) + l / 8, holding piece (slot ^ swizzle(row)). The
+  // swizzle of row 8g + l/8 is (4g + l/16) & 7, so the lane's part of the
+  // offset depends only on the parity of g; the row part is a scalar offset.
+  uint32_t lvoff[2];
 #pragma unroll
-    for (int p = 0; p < TL_LOADS_A; ++p) ra[p] = (va[p] && off + ca[p] < hch) ? ga[p][off] : z;
+  for (int par = 0; par < 2; ++par) {
+    const int piece = (lane % 8) ^ ((4 * par + lane / 16) & 7);
+    lvoff[par] = (uint32_t)(((lane / 8) * H + 8 * piece) * 2);
+  }
+  const uint32_t row8 = (uint32_t)(8 * H * 2);  // bytes of 8 rows
+  auto issue_stage = [&](int64_t kt, u32x4 *as, u32x4 *bs) {
+    const uint32_t soff = (uint32_t)(kt * TL_TK * 2);
 #pragma unroll
-    for (int p = 0; p < TL_LOADS_B; ++p) rb[p] = (vb[p] && off + cb[p] < hch) ? gb[p][off] : z;
-  };
-  auto store_stage = [&]() {
+    for (int u = 0; u < A_DMA; ++u) {
+      const int g = wave * A_DMA + u;
+      dma16(ar, &as[g * 64], lvoff[g & 1], soff + g * row8);
+    }
 #pragma unroll
-    for (int p = 0; p < TL_LOADS_A; ++p) As[la[p]] = ra[p];
-#pragma unroll
-    for (int p = 0; p < TL_LOADS_B; ++p) Bs[lb[p]] = rb[p];
+    for (int u = 0; u < B_DMA; ++u) {
+      const int g = wave * B_DMA + u;
+      dma16(br, &bs[g * 64], lvoff[g & 1], soff + g * row8);
+    }
   };
 
-  f32x4 acc[TL_FM][TL_FN];
+  f32x4 acc[FM][FN];
 #pragma unroll
-  for (int i = 0; i < TL_FM; ++i)
+  for (int i = 0; i < FM; ++i)
 #pragma unroll
-    for (int j = 0; j < TL_FN; ++j) acc[i][j] = zero4();
+    for (int j = 0; j < FN; ++j) acc[i][j] = zero4();
 
-  // H % 32 == 0 but not necessarily % 64: the last stage may hold one K-step.
-  const int64_t nsteps = H / KSTEP;
+  // H % 32 == 0 but not necessarily % 64: the last stage may hold one K-step
+  // (its second half is loaded but never read).
+  const int64_t nsteps = H / KSTEP;  // >= 1
   const int64_t nstages = (nsteps + 1) / 2;
 
-  load_stage(0);
-  store_stage();
-  __syncthreads();
-  for (int64_t kt = 0; kt < nstages; ++kt) {
-    if (kt + 1 < nstages) load_stage(kt + 1);
-    const int ks_here = (kt * 2 + 1 < nsteps) ? 2 : 1;
+  auto compute = [&](const u32x4 *as, const u32x4 *bs, int s) {
+    u32x4 a[FM], bb[FN];
 #pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      if (s < ks_here) {
-        u32x4 a[TL_FM], b[TL_FN];
+    for (int i = 0; i < FM; ++i) a[i] = as[tl_slot(wm * SM + 16 * i + li, 4 * s + lg)];
 #pragma unroll
-        for (int i = 0; i < TL_FM; ++i) a[i] = As[swz(wm * TL_WM + 16 * i + li, 4 * s + lg)];
+    for (int j = 0; j < FN; ++j) bb[j] = bs[tl_slot(wn * SN + 16 * j + li, 4 * s + lg)];
 #pragma unroll
-        for (int j = 0; j < TL_FN; ++j) b[j] = Bs[swz(wn * TL_WN + 16 * j + li, 4 * s + lg)];
+    for (int i = 0; i < FM; ++i)
 #pragma unroll
-        for (int i = 0; i < TL_FM; ++i)
-#pragma unroll
-          for (int j = 0; j < TL_FN; ++j) acc[i][j] = kstep(acc[i][j], a[i], b[j]);
-      }
-    }
+      for (int j = 0; j < FN; ++j) acc[i][j] = kstep(acc[i][j], a[i], bb[j]);
+  };
+
+  // Stages alternate between the two buffers; the loop body covers two stages
+  // and has no branches, the last one or two stages are peeled off.
+  issue_stage(0, As0, Bs0);
+  __syncthreads();  // waits for the direct loads (vmcnt) and meets the other waves
+  int64_t kt = 0;
+  for (; kt + 2 < nstages; kt += 2) {
+    issue_stage(kt + 1, As1, Bs1);
+    sched_fence();  // keep the loads ahead of the MFMAs they overlap with
+    compute(As0, Bs0, 0);
+    compute(As0, Bs0, 1);
+    __syncthreads();  // stage kt+1 landed; every wave is done with buffer 0
+    issue_stage(kt + 2, As0, Bs0);
+    sched_fence();
+    compute(As1, Bs1, 0);
+    compute(As1, Bs1, 1);
     __syncthreads();
-    if (kt + 1 < nstages) {
-      store_stage();
-      __syncthreads();
-    }
+  }
+  // one or two stages left; the very last may hold a single K-step (H % 64 == 32)
+  const bool last_full = (nsteps % 2) == 0;
+  if (kt + 1 < nstages) {
+    issue_stage(kt + 1, As1, Bs1);
+    sched_fence();
+    compute(As0, Bs0, 0);
+    compute(As0, Bs0, 1);
+    __syncthreads();
+    compute(As1, Bs1, 0);
+    if (last_full) compute(As1, Bs1, 1);
+  } else {
+    compute(As0, Bs0, 0);
+    if (last_full) compute(As0, Bs0, 1);
   }
 
-#pragma unroll
-  for (int j = 0; j < TL_FN; ++j) {
-    const int64_t col = n0 + wn * TL_WN + 16 * j + li;
-    if (col >= V) continue;
-#pragma unroll
-    for (int i = 0; i < TL_FM; ++i) {
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int64_t row = m0 + wm * TL_WM + 16 * i + 4 * lg + q;
-        if (row < M) store_out<OutT>(out, row * V + col, epilogue(acc[i][j][q], alpha, bias, col));
-      }
-    }
-  }
+  const int64_t rb = m0 + wm * SM;
+  store_blocks<FM, FN>([&](int i, int j) -> f32x4 & { return acc[i][j]; }, out, rb,
+                       M - rb < SM ? M - rb : SM, n0 + wn * SN, V, alpha, bias);
+}
+
+template <int TM, int WM, int WN, typename OutT>
+hipError_t launch_tm(const Bf16Args &a, hipStream_t stream) {
+  const int64_t tiles = ((a.M + TM - 1) / TM) * ((a.V + TL_TN - 1) / TL_TN);
+  hipLaunchKernelGGL((tiled_kernel<TM, WM, WN, OutT>), dim3((unsigned)tiles), dim3(64 * WM * WN), 0,
+                     stream, a.hidden, a.M, a.H, a.W, a.V, a.alpha, a.bias,
+                     static_cast<OutT *>(a.out));
+  return hipGetLastError();
+}
+
+template <typename OutT>
+hipError_t launch_t(const Bf16Args &a, hipStream_t stream) {
+  // 128-row tiles (four waves) when one of them covers M: no MFMA work on
+  // padding rows; else 256-row tiles (eight waves).
+  return a.M <= 128 ? launch_tm<128, 2, 4, OutT>(a, stream) : launch_tm<256, 4, 2, OutT>(a, stream);
 }
 
 }  // namespace
 
 hipError_t launch_tiled(const Bf16Args &a, hipStream_t stream) {
-  dim3 grid((unsigned)(((a.V + TL_BN - 1) / TL_BN) * ((a.M + TL_BM - 1) / TL_BM)));
-  dim3 block(TL_THREADS);
-  if (a.out_bf16)
-    hipLaunchKernelGGL((tiled_kernel<uint16_t>), grid, block, 0, stream, a.hidden, a.M, a.H, a.W,
-                       a.V, a.alpha, a.bias, static_cast<uint16_t *>(a.out));
-  else
-    hipLaunchKernelGGL((tiled_kernel<float>), grid, block, 0, stream, a.hidden, a.M, a.H, a.W, a.V,
-                       a.alpha, a.bias, static_cast<float *>(a.out));
-  return hipGetLastError();
+  return a.out_bf16 ? launch_t<uint16_t>(a, stream) : launch_t<float>(a, stream);
 }
 
 }  // namespace lmhead

@@ -43,7 +43,9 @@ def test_status_strings_and_version():
     (-1, 4096, 10, False), (4, 0, 10, False), (4, 4096, 0, False),
     ((1 << 24) + 1, 32, 10, False),  # beyond LMHEAD_MAX_M
     (4, (1 << 16) + 32, 10, False),  # beyond LMHEAD_MAX_H
-    (1 << 24, 32, 1 << 20, False),   # M * V beyond 2^42
+    (4, 32, (1 << 20) + 1, False),   # beyond LMHEAD_MAX_V
+    (4, 32, 1 << 20, True),
+    (1 << 24, 32, 1 << 19, False),   # M * V beyond 2^42
 ])
 def test_shape_ok(M, H, V, ok):
     assert L.shape_ok(M, H, V) is ok
