@@ -56,10 +56,16 @@ def flops(M, H, V):
     return 2 * M * H * V
 
 
-def kernel_source_hash():
+# Sources the decode kernel's code and launch depend on: a counter reading is
+# valid only while these are unchanged.
+DECODE_SOURCES = ("kstep.hpp", "launch.hpp", "lmhead_api.cpp", "skinny.hip")
+
+
+def kernel_source_hash(files=DECODE_SOURCES):
     h = hashlib.sha256()
-    for p in sorted((ROOT / "lm_head_logits_amd" / "csrc").glob("*")):
-        h.update(p.name.encode())
+    for name in files:
+        p = ROOT / "lm_head_logits_amd" / "csrc" / name
+        h.update(name.encode())
         h.update(p.read_bytes())
     return h.hexdigest()[:16]
 
@@ -199,6 +205,18 @@ def bench_nvfp4(torch, L, wl, dev, warmup, steps, copies=4):
     return res
 
 
+def bench_copy(torch, dev, warmup, steps, nbytes=1 << 30):
+    """A plain device-to-device copy of `nbytes` (torch's copy kernel): reads
+    and writes exactly nbytes, so the HBM counters read on it give the scale
+    factor from counter units to bytes."""
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    _, _, per = timed_calls(torch, [lambda: dst.copy_(src)], warmup, steps)
+    us = 1e3 * float(np.mean(per[0]))
+    return {"bytes_read": nbytes, "bytes_written": nbytes, "us_avg": round(us, 1),
+            "GBps": round(2 * nbytes / us / 1e3, 1)}
+
+
 # ----------------------------------------------------------------------------
 # CPU baseline: the oracle on a bounded sample of the decode workload.
 # ----------------------------------------------------------------------------
@@ -241,8 +259,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--only", choices=["decode", "prefill", "spec", "nvfp4", "all"], default="all",
-                    help="run one workload only (for profiling); the headline line needs decode")
+    ap.add_argument("--only", choices=["decode", "prefill", "spec", "nvfp4", "copy", "all"], default="all",
+                    help="run one workload only (for profiling; 'copy' is the HBM counter "
+                         "calibration); the headline line needs decode")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -262,7 +281,8 @@ def main():
         # a single non-headline workload, for profiling: print its numbers only
         fn = {"prefill": lambda: bench_prefill(torch, L, wl, dev, args.warmup, args.steps),
               "spec": lambda: bench_spec(torch, L, wl, dev, args.warmup, args.steps),
-              "nvfp4": lambda: bench_nvfp4(torch, L, wl, dev, args.warmup, args.steps)}[args.only]
+              "nvfp4": lambda: bench_nvfp4(torch, L, wl, dev, args.warmup, args.steps),
+              "copy": lambda: bench_copy(torch, dev, args.warmup, args.steps)}[args.only]
         print(json.dumps({"workload": args.only, "result": fn()}), flush=True)
         return
     dec = bench_decode(torch, L, wl, dev, args.warmup, args.steps)
