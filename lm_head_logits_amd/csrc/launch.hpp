@@ -29,6 +29,23 @@ struct Nvfp4Args {
   uint16_t *out;           // [M, V] bf16
 };
 
+// Compute units of the current device (queried once per device).
+int device_cus();
+
+// Split of `ncb` vocabulary column blocks (16 weight rows each) over the
+// waves of a weight-streaming kernel with `waves` waves per work-group: `nvs`
+// work-groups along V, each wave owning at most `nb` consecutive blocks. The
+// weight stream's bandwidth grows with the number of CUs streaming, so the
+// grid is one work-group per CU (fewer when V is small), with the blocks
+// spread evenly: every wave owns floor or ceil of ncb / (nvs * waves) blocks
+// (the kernels derive their own range from the grid size). Past nb_max blocks
+// per wave the grid grows instead (several work-groups per CU).
+struct VSplit {
+  int64_t nvs;
+  int nb;
+};
+VSplit vsplit(int64_t ncb, int waves, int nb_max);
+
 hipError_t launch_skinny(const Bf16Args &a, hipStream_t stream);
 hipError_t launch_tiled(const Bf16Args &a, hipStream_t stream);
 hipError_t launch_nvfp4(const Nvfp4Args &a, hipStream_t stream);

@@ -9,6 +9,8 @@
 
 #include <hip/hip_runtime.h>
 
+#include <atomic>
+
 #include "launch.hpp"
 
 namespace {
@@ -29,6 +31,34 @@ lmhead_status check_shape(int64_t M, int64_t H, int64_t V) {
 int auto_path(int64_t M) { return M <= 64 ? LMHEAD_PATH_SKINNY : LMHEAD_PATH_TILED; }
 
 }  // namespace
+
+namespace lmhead {
+
+int device_cus() {
+  constexpr int CACHED = 64;
+  static std::atomic<int> cache[CACHED];  // zero: not queried yet
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 256;
+  if (dev >= 0 && dev < CACHED && (cus = cache[dev].load(std::memory_order_relaxed)) > 0) return cus;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+    return 256;  // the MI355X count; only the balance of the split depends on it
+  if (dev >= 0 && dev < CACHED) cache[dev].store(cus, std::memory_order_relaxed);
+  return cus;
+}
+
+VSplit vsplit(int64_t ncb, int waves, int nb_max) {
+  const int64_t cus = device_cus();
+  int64_t nvs = (ncb + waves - 1) / waves;  // at least one block per wave
+  if (nvs > cus) nvs = cus;
+  int64_t nb = (ncb + nvs * waves - 1) / (nvs * waves);
+  if (nb > nb_max) {
+    nb = nb_max;
+    nvs = (ncb + nb * waves - 1) / (nb * waves);
+  }
+  return VSplit{nvs, (int)nb};
+}
+
+}  // namespace lmhead
 
 extern "C" {
 

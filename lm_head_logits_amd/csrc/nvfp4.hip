@@ -14,7 +14,6 @@
 // K-step chain of kstep.hpp runs unchanged. So this kernel's logits equal
 // lmhead_logits on the dequantised weight with alpha = fl32(g * alpha), bit
 // for bit.
-#include <atomic>
 #include <type_traits>
 
 #include "kstep.hpp"
@@ -173,7 +172,10 @@ hipError_t launch_generic_r(const Nvfp4Args &a, hipStream_t stream) {
 // rows come through LDS as in the bf16 weight-streaming kernel, eight waves
 // per work-group held in lockstep by one LDS barrier per quad.
 // ---------------------------------------------------------------------------
-constexpr int NS_WAVES = 8;
+#ifndef LMHEAD_NS_WAVES
+#define LMHEAD_NS_WAVES 8
+#endif
+constexpr int NS_WAVES = LMHEAD_NS_WAVES;
 constexpr int NS_THREADS = 64 * NS_WAVES;
 constexpr int NS_KC = 128;          // K per quad == K per LDS chunk of hidden
 constexpr int NS_CPR = NS_KC / 8;   // 16-byte hidden pieces per row per chunk
@@ -181,6 +183,10 @@ constexpr int NS_CPR = NS_KC / 8;   // 16-byte hidden pieces per row per chunk
 #define LMHEAD_NS_P 2
 #endif
 constexpr int NS_P = LMHEAD_NS_P;   // quads of weight loads in flight ahead of use
+#ifndef LMHEAD_NS_NB_MAX
+#define LMHEAD_NS_NB_MAX 6
+#endif
+constexpr int NS_NB_MAX = LMHEAD_NS_NB_MAX;  // column blocks per wave
 
 constexpr int NS_SEGQ = 16;                 // quads per LDS segment of block scales
 constexpr int NS_SROW = NS_SEGQ + 1;        // 8-byte LDS words per weight row (1 word pad: banks)
@@ -241,23 +247,30 @@ __global__ __launch_bounds__(NS_THREADS, 1) void nvfp4_stream_kernel(
   const int lg = lane >> 4;
   const int64_t nmb = (M + 63) / 64;
   const int64_t m0 = ((int64_t)blockIdx.x % nmb) * 64;
-  const int64_t cb0 = (((int64_t)blockIdx.x / nmb) * NS_WAVES + wave) * NB;
-  const bool active = cb0 * 16 < V;
+  // Column blocks [cb0, cb1) of this wave: the ncb blocks split evenly over
+  // the grid's waves along V (at most NB each), as in the bf16 kernel.
+  const int64_t ncb = (V + 15) / 16;
+  const int64_t tw = (int64_t)(gridDim.x / nmb) * NS_WAVES;
+  const int64_t g0 = ((int64_t)blockIdx.x / nmb) * NS_WAVES;  // the work-group's first wave
+  const int64_t cb0 = (g0 + wave) * ncb / tw, cb1 = (g0 + wave + 1) * ncb / tw;
+  const bool active = cb1 > cb0;
+  const int64_t cend = cb1 * 16 < V ? cb1 * 16 : V;
 
   const int64_t HC = H / 2, HS = H / 16;  // code and scale bytes per weight row
-  const int64_t wrows = V - cb0 * 16 < NB * 16 ? V - cb0 * 16 : NB * 16;
   const int64_t base_row = active ? cb0 * 16 : 0;
-  const rsrc_t cr = make_rsrc(codes + base_row * HC, active ? (uint32_t)(wrows * HC) : 0u);
+  const rsrc_t cr = make_rsrc(codes + base_row * HC, active ? (uint32_t)((cend - cb0 * 16) * HC) : 0u);
   const uint32_t cvoff = (uint32_t)(li * HC + 16 * lg);
   const uint32_t cjs = (uint32_t)(16 * HC);
   // scale byte of K-step t of a quad for this lane group: 2t + lg/2
   const uint32_t ssel = (lg >> 1) ? 0x07050301u : 0x06040200u;
 
-  // Block scales: the work-group's WROWS weight rows are contiguous in memory;
-  // each segment of NS_SEGQ quads (8 scale bytes per row per quad) is loaded
-  // cooperatively into LDS, so the scale stream is read once, in order.
-  const int64_t wg_row0 = ((int64_t)blockIdx.x / nmb) * WROWS;
-  const int64_t wg_rows = V - wg_row0 < WROWS ? V - wg_row0 : WROWS;
+  // Block scales: the work-group's weight rows (at most WROWS) are contiguous
+  // in memory; each segment of NS_SEGQ quads (8 scale bytes per row per quad)
+  // is loaded cooperatively into LDS, so the scale stream is read once, in
+  // order.
+  const int64_t wg_cb0 = g0 * ncb / tw, wg_cb1 = (g0 + NS_WAVES) * ncb / tw;
+  const int64_t wg_row0 = wg_cb0 * 16;
+  const int64_t wg_rows = (wg_cb1 * 16 < V ? wg_cb1 * 16 : V) - wg_row0;
   const rsrc_t sr = make_rsrc(scales + wg_row0 * HS, (uint32_t)(wg_rows * HS));
   const int64_t nq = H / NS_KC;
   // Scale piece i of this thread in segment `seg`: its load offset (pieces past
@@ -288,7 +301,7 @@ __global__ __launch_bounds__(NS_THREADS, 1) void nvfp4_stream_kernel(
     }
   };
   // LDS row of this lane's weight row in column block j
-  const int srow0 = (wave * NB * 16 + li) * NS_SROW;
+  const int srow0 = (int)((cb0 - wg_cb0) * 16 + li) * NS_SROW;
 
   const int64_t hrows = M - m0 < 64 ? M - m0 : 64;
   const rsrc_t hr = make_rsrc(hidden + m0 * H, (uint32_t)(hrows * H * 2));
@@ -388,43 +401,29 @@ __global__ __launch_bounds__(NS_THREADS, 1) void nvfp4_stream_kernel(
 
   if (!active) return;
   store_blocks<R, NB>([&](int i, int j) -> f32x4 & { return acc[j][i]; }, out, m0,
-                      M - m0 < 16 * R ? M - m0 : 16 * R, cb0 * 16, V, scale, bias);
+                      M - m0 < 16 * R ? M - m0 : 16 * R, cb0 * 16, cend, V, scale, bias);
 }
 
 template <int R, int NB>
-int64_t ns_resident_slots() {
-  static std::atomic<int64_t> cached{0};
-  int64_t v = cached.load(std::memory_order_relaxed);
-  if (v == 0) {
-    int dev = 0, cus = 0, per_cu = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, nvfp4_stream_kernel<R, NB>,
-                                                     NS_THREADS, 0) != hipSuccess ||
-        cus <= 0 || per_cu <= 0)
-      return 256;
-    v = (int64_t)cus * per_cu;
-    cached.store(v, std::memory_order_relaxed);
-  }
-  return v;
-}
-
-template <int R, int NB>
-hipError_t launch_stream_nb(const Nvfp4Args &a, hipStream_t stream) {
-  const int64_t ncb = (a.V + 15) / 16;
-  const int64_t nvs = (ncb + NS_WAVES * NB - 1) / (NS_WAVES * NB);
+hipError_t launch_stream_nb(const Nvfp4Args &a, int64_t nvs, hipStream_t stream) {
   dim3 grid((unsigned)(nvs * ((a.M + 63) / 64)));
   hipLaunchKernelGGL((nvfp4_stream_kernel<R, NB>), grid, dim3(NS_THREADS), 0, stream, a.hidden,
                      a.M, a.H, a.codes, a.scales, a.V, a.scale, a.bias, a.out);
   return hipGetLastError();
 }
 
+// The variant with NB = the split's blocks per wave (NB <= NBM).
+template <int R, int NBM>
+hipError_t launch_stream_split(const Nvfp4Args &a, const VSplit &sp, hipStream_t stream) {
+  if constexpr (NBM > 1) {
+    if (sp.nb < NBM) return launch_stream_split<R, NBM - 1>(a, sp, stream);
+  }
+  return launch_stream_nb<R, NBM>(a, sp.nvs, stream);
+}
+
 template <int R>
 hipError_t launch_stream_r(const Nvfp4Args &a, hipStream_t stream) {
-  const int64_t ncb = (a.V + 15) / 16;
-  if ((ncb + 4 * NS_WAVES - 1) / (4 * NS_WAVES) <= ns_resident_slots<R, 4>())
-    return launch_stream_nb<R, 4>(a, stream);
-  return launch_stream_nb<R, 5>(a, stream);
+  return launch_stream_split<R, NS_NB_MAX>(a, vsplit((a.V + 15) / 16, NS_WAVES, NS_NB_MAX), stream);
 }
 
 }  // namespace

@@ -13,18 +13,20 @@
 //
 // Measured on MI355X (HBM read of the 1.05 GB decode weight): the order in
 // which the GPU as a whole walks the weight decides the bandwidth. Waves that
-// drift apart in K reach ~4.8 TB/s; eight waves per work-group held in
-// lockstep by the per-chunk LDS barrier (512 consecutive weight rows at the
+// drift apart in K reach ~4.8 TB/s; the waves of a work-group held in
+// lockstep by the per-chunk LDS barrier (~512 consecutive weight rows at the
 // same K) reach ~5.8 TB/s. The barrier is an LDS-only barrier so prefetched
-// weight loads stay in flight across it.
+// weight loads stay in flight across it. Sixteen waves of two column blocks
+// with 64-element chunks and a two-step prefetch beat eight waves of four
+// blocks with 128-element chunks by 2-4% (decode, M = 1..64).
 //
-// Launch: the host picks NB so that every wave of the grid is resident at
-// once (a second, partial round of waves would stream at a fraction of the
-// bandwidth). Grid (1-D): vocabulary slices of WAVES * NB column blocks,
-// times 64-row blocks of M (one for M <= 64; the forced-path test drives
-// more).
-#include <atomic>
-
+// Launch: one work-group per CU, the vocabulary's column blocks split evenly
+// over all waves (each owns floor or ceil of the mean, NB = the ceiling).
+// Measured: the stream's bandwidth follows the number of CUs streaming, and a
+// CU that holds two work-groups while others hold one finishes last (at
+// V = 151936: 297 work-groups of 32 blocks took 1.4x as long as 238 of 40).
+// Grid (1-D): vocabulary slices times 64-row blocks of M (one for M <= 64;
+// the forced-path test drives more).
 #include "kstep.hpp"
 #include "launch.hpp"
 
@@ -33,10 +35,10 @@ namespace lmhead {
 namespace {
 
 #ifndef LMHEAD_SK_WAVES
-#define LMHEAD_SK_WAVES 8
+#define LMHEAD_SK_WAVES 16
 #endif
 #ifndef LMHEAD_SK_KC
-#define LMHEAD_SK_KC 128
+#define LMHEAD_SK_KC 64
 #endif
 constexpr int SK_WAVES = LMHEAD_SK_WAVES;
 constexpr int SK_THREADS = 64 * SK_WAVES;
@@ -44,12 +46,17 @@ constexpr int SK_KC = LMHEAD_SK_KC;     // K elements per LDS chunk of hidden (o
 constexpr int SK_SPC = SK_KC / KSTEP;   // K-steps per chunk
 constexpr int SK_CPR = SK_KC / 8;       // 16-byte pieces per hidden row per chunk
 #ifndef LMHEAD_SK_P
-#define LMHEAD_SK_P 4
+#define LMHEAD_SK_P 2
 #endif
 #ifndef LMHEAD_SK_POLICY
 #define LMHEAD_SK_POLICY LOAD_DEFAULT
 #endif
 constexpr int SK_P = LMHEAD_SK_P;       // weight prefetch depth, in K-steps (divides SK_SPC)
+// Column blocks per wave at most: with 16 waves per CU a wave has 128 VGPRs,
+// which hold 4 * NB * R accumulators and 4 * P * NB weight registers without
+// spilling up to NB = 4 (R <= 3) or NB = 3 (R = 4).
+template <int R>
+constexpr int sk_nb_max() { return R >= 4 ? 3 : 4; }
 // Cache policy of the weight stream. Measured on MI355X: the non-temporal
 // hint makes this access pattern about 1.5x slower, so the default policy.
 constexpr int SK_POLICY = LMHEAD_SK_POLICY;
@@ -76,15 +83,20 @@ __global__ __launch_bounds__(SK_THREADS, SK_WAVES >= 8 ? 1 : 2) void skinny_kern
   const int lg = lane >> 4;
   const int64_t nmb = (M + 63) / 64;
   const int64_t m0 = ((int64_t)blockIdx.x % nmb) * 64;
-  const int64_t cb0 = (((int64_t)blockIdx.x / nmb) * SK_WAVES + wave) * NB;  // first column block
-  const bool active = cb0 * 16 < V;  // wave-uniform
+  // This wave's column blocks [cb0, cb1): the ncb blocks split evenly over
+  // all waves of the grid along V, at most NB each (the host sized NB so).
+  const int64_t ncb = (V + 15) / 16;
+  const int64_t tw = (int64_t)(gridDim.x / nmb) * SK_WAVES;
+  const int64_t g = ((int64_t)blockIdx.x / nmb) * SK_WAVES + wave;
+  const int64_t cb0 = g * ncb / tw, cb1 = (g + 1) * ncb / tw;
+  const bool active = cb1 > cb0;  // wave-uniform
+  const int64_t cend = cb1 * 16 < V ? cb1 * 16 : V;  // end of this wave's columns
 
-  // Weight: one buffer resource per wave over its NB * 16 rows (rows past V
-  // read as zero); lane offset li*H + 8*lg elements, column block j at
-  // j*16*H elements (a scalar offset), K-step s at 32*s elements.
-  const int64_t wrows = V - cb0 * 16 < NB * 16 ? V - cb0 * 16 : NB * 16;
+  // Weight: one buffer resource per wave over its rows [16 cb0, cend)
+  // (blocks j >= cb1 - cb0 read as zero); lane offset li*H + 8*lg elements,
+  // column block j at j*16*H elements (a scalar offset), K-step s at 32*s.
   const rsrc_t wr = make_rsrc(W + (active ? cb0 * 16 : 0) * H,
-                              active ? (uint32_t)(wrows * H * 2) : 0u);
+                              active ? (uint32_t)((cend - cb0 * 16) * H * 2) : 0u);
   const uint32_t wvoff = (uint32_t)((li * H + 8 * lg) * 2);
   const uint32_t wjstride = (uint32_t)(16 * H * 2);
 
@@ -185,48 +197,30 @@ __global__ __launch_bounds__(SK_THREADS, SK_WAVES >= 8 ? 1 : 2) void skinny_kern
   if (!active) return;
   // acc is indexed [column block][row block]
   store_blocks<R, NB>([&](int i, int j) -> f32x4 & { return acc[j][i]; }, out, m0,
-                      M - m0 < 16 * R ? M - m0 : 16 * R, cb0 * 16, V, alpha, bias);
-}
-
-// Work-groups of one kernel variant resident on the device at once, queried
-// once per variant (the library's only cached state; every GPU it runs on is
-// taken to be the same model).
-template <int R, int NB, typename OutT>
-int64_t resident_slots() {
-  static std::atomic<int64_t> cached{0};
-  int64_t v = cached.load(std::memory_order_relaxed);
-  if (v == 0) {
-    int dev = 0, cus = 0, per_cu = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, skinny_kernel<R, NB, OutT>,
-                                                     SK_THREADS, 0) != hipSuccess ||
-        cus <= 0 || per_cu <= 0)
-      return 256;  // conservative: one work-group per CU of a 256-CU part
-    v = (int64_t)cus * per_cu;
-    cached.store(v, std::memory_order_relaxed);
-  }
-  return v;
+                      M - m0 < 16 * R ? M - m0 : 16 * R, cb0 * 16, cend, V, alpha, bias);
 }
 
 template <int R, int NB, typename OutT>
-hipError_t launch_nb(const Bf16Args &a, hipStream_t stream) {
-  const int64_t ncb = (a.V + 15) / 16;
-  const int64_t nvs = (ncb + SK_WAVES * NB - 1) / (SK_WAVES * NB);
+hipError_t launch_nb(const Bf16Args &a, int64_t nvs, hipStream_t stream) {
   dim3 grid((unsigned)(nvs * ((a.M + 63) / 64)));
   hipLaunchKernelGGL((skinny_kernel<R, NB, OutT>), grid, dim3(SK_THREADS), 0, stream, a.hidden,
                      a.M, a.H, a.W, a.V, a.alpha, a.bias, static_cast<OutT *>(a.out));
   return hipGetLastError();
 }
 
-// NB = 4 (more, smaller waves) when that grid is resident in one round, else
-// NB = 5 (one round up to V = 163840 at two work-groups per CU).
+// The variant with NB = the split's blocks per wave (NB <= NBM).
+template <int R, int NBM, typename OutT>
+hipError_t launch_split(const Bf16Args &a, const VSplit &sp, hipStream_t stream) {
+  if constexpr (NBM > 1) {
+    if (sp.nb < NBM) return launch_split<R, NBM - 1, OutT>(a, sp, stream);
+  }
+  return launch_nb<R, NBM, OutT>(a, sp.nvs, stream);
+}
+
 template <int R, typename OutT>
 hipError_t launch_r(const Bf16Args &a, hipStream_t stream) {
-  const int64_t ncb = (a.V + 15) / 16;
-  if ((ncb + 4 * SK_WAVES - 1) / (4 * SK_WAVES) <= resident_slots<R, 4, OutT>())
-    return launch_nb<R, 4, OutT>(a, stream);
-  return launch_nb<R, 5, OutT>(a, stream);
+  constexpr int NBM = sk_nb_max<R>();
+  return launch_split<R, NBM, OutT>(a, vsplit((a.V + 15) / 16, SK_WAVES, NBM), stream);
 }
 
 template <typename OutT>

@@ -180,7 +180,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void tiled_kernel(const uint16_t *
 
   const int64_t rb = m0 + wm * SM;
   store_blocks<FM, FN>([&](int i, int j) -> f32x4 & { return acc[i][j]; }, out, rb,
-                       M - rb < SM ? M - rb : SM, n0 + wn * SN, V, alpha, bias);
+                       M - rb < SM ? M - rb : SM, n0 + wn * SN, V, V, alpha, bias);
 }
 
 template <int TM, int WM, int WN, typename OutT>
