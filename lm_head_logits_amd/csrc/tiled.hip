@@ -6,10 +6,11 @@
 // with no fp32 copy of either operand) with the alpha of vLLM PR 49120
 // folded into the epilogue (section "muP is folded into the fp32 GEMM").
 //
-// Work-group tile TM x 256 output elements with eight waves: TM = 256 in a
-// 4 x 2 arrangement (64 x 128 per wave), or TM = 128 (when that covers M) in
-// 2 x 4 (64 x 64 per wave). Each wave's 16 x 16 MFMA blocks keep their fp32
-// accumulators in registers for the whole K loop. K is staged through LDS 64 elements at a time, double-buffered:
+// Work-group tile 256 x 256 output elements with eight waves in a 4 x 2
+// arrangement (64 x 128 per wave), or 128 x 128 with four 64 x 64 waves when
+// M <= 128. Each wave's 16 x 16 MFMA blocks keep their fp32 accumulators in
+// registers for the whole K loop. K is staged through LDS 64 elements at a
+// time, double-buffered:
 // the loads of stage k+1 are issued as direct-to-LDS buffer loads
 // (buffer_load_dwordx4 ... lds, no registers) before the MFMAs of stage k run,
 // and one barrier per stage hands the buffers over. Every output element is
@@ -34,7 +35,6 @@ namespace lmhead {
 
 namespace {
 
-constexpr int TL_TN = 256;
 constexpr int TL_TK = 64;                 // two K-steps per LDS stage
 constexpr int TL_PPR = TL_TK / 8;         // 16-byte pieces per row per stage
 constexpr int TL_XCDS = 8;
@@ -54,7 +54,7 @@ __device__ __forceinline__ void dma16(rsrc_t r, void *dst, uint32_t voff, uint32
 // WM x WN waves; each owns a (TM / WM) x (TN / WN) sub-tile of at most 4 x 8
 // MFMA blocks: <= 128 fp32 accumulators per lane, which the compiler keeps in
 // ordinary VGPRs next to the operand fragments (two waves per SIMD).
-template <int TM, int WM, int WN, typename OutT>
+template <int TM, int TN, int WM, int WN, typename OutT>
 __global__ __launch_bounds__(64 * WM * WN, 1) void tiled_kernel(const uint16_t *__restrict__ hidden,
                                                                int64_t M, int64_t H,
                                                                const uint16_t *__restrict__ W,
@@ -62,17 +62,17 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void tiled_kernel(const uint16_t *
                                                                const float *__restrict__ bias,
                                                                OutT *__restrict__ out) {
   constexpr int NW = WM * WN;
-  constexpr int SM = TM / WM, SN = TL_TN / WN;   // wave sub-tile
+  constexpr int SM = TM / WM, SN = TN / WN;   // wave sub-tile
   constexpr int FM = SM / 16;                    // 16-row blocks per wave
   constexpr int FN = SN / 16;                    // 16-column blocks per wave
   constexpr int A_DMA = TM * TL_PPR / 64 / NW;     // direct loads per wave per stage (A)
-  constexpr int B_DMA = TL_TN * TL_PPR / 64 / NW;  // (B)
-  static_assert(A_DMA * 64 * NW == TM * TL_PPR && B_DMA * 64 * NW == TL_TN * TL_PPR, "tiling");
+  constexpr int B_DMA = TN * TL_PPR / 64 / NW;  // (B)
+  static_assert(A_DMA * 64 * NW == TM * TL_PPR && B_DMA * 64 * NW == TN * TL_PPR, "tiling");
   // Two separately declared buffers per operand (not one array indexed by a
   // variable), so the compiler can tell the stage being loaded from the stage
   // being read and does not wait for the former before reading the latter.
   __shared__ u32x4 As0[TM * TL_PPR], As1[TM * TL_PPR];
-  __shared__ u32x4 Bs0[TL_TN * TL_PPR], Bs1[TL_TN * TL_PPR];
+  __shared__ u32x4 Bs0[TN * TL_PPR], Bs1[TN * TL_PPR];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -84,16 +84,16 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void tiled_kernel(const uint16_t *
 
   // XCD-aware tile index, M-tiles fastest.
   const int64_t nmt = (M + TM - 1) / TM;
-  const int64_t ntiles = nmt * ((V + TL_TN - 1) / TL_TN);
+  const int64_t ntiles = nmt * ((V + TN - 1) / TN);
   const int64_t b = blockIdx.x;
   const int64_t q = ntiles / TL_XCDS, r = ntiles % TL_XCDS;
   const int64_t xcd = b % TL_XCDS, pos = b / TL_XCDS;
   const int64_t t = xcd < r ? xcd * (q + 1) + pos : r * (q + 1) + (xcd - r) * q + pos;
   const int64_t m0 = (t % nmt) * TM;
-  const int64_t n0 = (t / nmt) * TL_TN;
+  const int64_t n0 = (t / nmt) * TN;
 
   const int64_t arows = M - m0 < TM ? M - m0 : TM;
-  const int64_t brows = V - n0 < TL_TN ? V - n0 : TL_TN;
+  const int64_t brows = V - n0 < TN ? V - n0 : TN;
   const rsrc_t ar = make_rsrc(hidden + m0 * H, (uint32_t)(arows * H * 2));
   const rsrc_t br = make_rsrc(W + n0 * H, (uint32_t)(brows * H * 2));
 
@@ -183,10 +183,10 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void tiled_kernel(const uint16_t *
                        M - rb < SM ? M - rb : SM, n0 + wn * SN, V, V, alpha, bias);
 }
 
-template <int TM, int WM, int WN, typename OutT>
+template <int TM, int TN, int WM, int WN, typename OutT>
 hipError_t launch_tm(const Bf16Args &a, hipStream_t stream) {
-  const int64_t tiles = ((a.M + TM - 1) / TM) * ((a.V + TL_TN - 1) / TL_TN);
-  hipLaunchKernelGGL((tiled_kernel<TM, WM, WN, OutT>), dim3((unsigned)tiles), dim3(64 * WM * WN), 0,
+  const int64_t tiles = ((a.M + TM - 1) / TM) * ((a.V + TN - 1) / TN);
+  hipLaunchKernelGGL((tiled_kernel<TM, TN, WM, WN, OutT>), dim3((unsigned)tiles), dim3(64 * WM * WN), 0,
                      stream, a.hidden, a.M, a.H, a.W, a.V, a.alpha, a.bias,
                      static_cast<OutT *>(a.out));
   return hipGetLastError();
@@ -194,9 +194,11 @@ hipError_t launch_tm(const Bf16Args &a, hipStream_t stream) {
 
 template <typename OutT>
 hipError_t launch_t(const Bf16Args &a, hipStream_t stream) {
-  // 128-row tiles (four waves) when one of them covers M: no MFMA work on
-  // padding rows; else 256-row tiles (eight waves).
-  return a.M <= 128 ? launch_tm<128, 2, 4, OutT>(a, stream) : launch_tm<256, 4, 2, OutT>(a, stream);
+  // M <= 128: 128 x 128 tiles of four 64 x 64 waves (one tile covers M, and
+  // the twice as many tiles fill the CUs better: measured 3-6% faster than
+  // 128 x 256 at M = 128). Larger M: 256 x 256 tiles of eight 64 x 128 waves.
+  return a.M <= 128 ? launch_tm<128, 128, 2, 2, OutT>(a, stream)
+                    : launch_tm<256, 256, 4, 2, OutT>(a, stream);
 }
 
 }  // namespace
