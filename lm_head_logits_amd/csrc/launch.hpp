@@ -49,5 +49,6 @@ VSplit vsplit(int64_t ncb, int waves, int nb_max);
 hipError_t launch_skinny(const Bf16Args &a, hipStream_t stream);
 hipError_t launch_tiled(const Bf16Args &a, hipStream_t stream);
 hipError_t launch_nvfp4(const Nvfp4Args &a, hipStream_t stream);
+hipError_t launch_tiled_nvfp4(const Nvfp4Args &a, hipStream_t stream);
 
 }  // namespace lmhead

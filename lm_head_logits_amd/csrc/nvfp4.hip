@@ -18,6 +18,7 @@
 
 #include "kstep.hpp"
 #include "launch.hpp"
+#include "nvfp4_decode.hpp"
 
 namespace lmhead {
 
@@ -205,21 +206,6 @@ __device__ __forceinline__ void transpose4(uint32_t &x0, uint32_t &x1, uint32_t 
   x1 = c[1];
   x2 = d[0];
   x3 = d[1];
-}
-
-// Eight codes (element 2p in the low nibble of byte p) times the block scale
-// -> eight exact bf16 weights in MFMA slot order.
-template <int P>
-__device__ __forceinline__ uint32_t dequant_pair(uint32_t codes, float s) {
-  const auto v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 1.0f, P);
-  const uint32_t lo = __builtin_bit_cast(uint32_t, v[0] * s);
-  const uint32_t hi = __builtin_bit_cast(uint32_t, v[1] * s);
-  return __builtin_amdgcn_perm(hi, lo, 0x07060302u);  // upper halves: (lo.bf16, hi.bf16)
-}
-
-__device__ __forceinline__ u32x4 dequant8_fast(uint32_t codes, float s) {
-  return u32x4{dequant_pair<0>(codes, s), dequant_pair<1>(codes, s), dequant_pair<2>(codes, s),
-               dequant_pair<3>(codes, s)};
 }
 
 template <int R, int NB>
@@ -429,6 +415,9 @@ hipError_t launch_stream_r(const Nvfp4Args &a, hipStream_t stream) {
 }  // namespace
 
 hipError_t launch_nvfp4(const Nvfp4Args &a, hipStream_t stream) {
+  // More than one 64-row block: the tiled kernel decodes each weight element
+  // once per 256-row tile instead of once per 64-row block.
+  if (a.M > 64) return launch_tiled_nvfp4(a, stream);
   const int64_t rows = a.M < 64 ? a.M : 64;
   const int rb = (int)((rows + 15) / 16);
   // the streaming kernel reads 8 scale bytes at a time: rows of 8k bytes on an

@@ -189,8 +189,11 @@ def test_nvfp4_nibble_order_on_gpu():
         assert host_bits(out)[0, 0] == want
 
 
+# M <= 64 runs the weight-streaming NVFP4 kernel, M > 64 the tiled kernel with
+# the decode in its B stage (128-row tiles: 129 and 300 leave ragged tiles;
+# H = 96 and 160 end in a half stage).
 @pytest.mark.parametrize("M,H,V", [(1, 32, 1), (4, 64, 100), (64, 256, 1000), (65, 96, 333),
-                                   (200, 512, 2049)])
+                                   (129, 160, 515), (200, 512, 2049), (300, 128, 1000)])
 def test_nvfp4_parity_and_equals_bf16_path(M, H, V):
     rng = np.random.default_rng(M + H + V)
     say(f"nvfp4 M={M} H={H} V={V}")
