@@ -7,8 +7,8 @@
 // folded into the epilogue (section "muP is folded into the fp32 GEMM").
 //
 // Work-group tile 256 x 256 output elements with eight waves in a 4 x 2
-// arrangement (64 x 128 per wave), or 128 x 128 with four 64 x 64 waves when
-// M <= 128. Each wave's 16 x 16 MFMA blocks keep their fp32 accumulators in
+// arrangement (64 x 128 per wave), or 128 x 128 / 128 x 160 with four waves of
+// 64 x 64 / 64 x 80 when M <= 128. Each wave's 16 x 16 MFMA blocks keep their fp32 accumulators in
 // registers for the whole K loop. K is staged through LDS 64 elements at a
 // time, double-buffered:
 // the loads of stage k+1 are issued as direct-to-LDS buffer loads
@@ -260,11 +260,17 @@ hipError_t launch_tm(const TiledArgs &a, hipStream_t stream) {
 
 template <typename OutT>
 hipError_t launch_t(const TiledArgs &a, hipStream_t stream) {
-  // M <= 128: 128 x 128 tiles of four 64 x 64 waves (one tile covers M, and
-  // the twice as many tiles fill the CUs better: measured 3-6% faster than
-  // 128 x 256 at M = 128). Larger M: 256 x 256 tiles of eight 64 x 128 waves.
-  return a.M <= 128 ? launch_tm<128, 128, 2, 2, false, OutT>(a, stream)
-                    : launch_tm<256, 256, 4, 2, false, OutT>(a, stream);
+  if (a.M > 128) return launch_tm<256, 256, 4, 2, false, OutT>(a, stream);
+  // M <= 128: one 128-row tile covers M; four waves (2 x 2), two tiles
+  // resident per CU. The tile width (128 or 160) is the one
+  // with the smaller (rounds of resident tiles) x width, since a partial last
+  // round costs a whole round: at V = 151936, 160 gives 950 tiles (2 rounds
+  // of 512) against 1187 (3 rounds), measured 8-11% faster; at V = 128256,
+  // 128 gives 1002 tiles (2 rounds).
+  const int64_t slots = 2 * (int64_t)device_cus();
+  auto cost = [&](int64_t tn) { return ((a.V + tn - 1) / tn + slots - 1) / slots * tn; };
+  return cost(160) < cost(128) ? launch_tm<128, 160, 2, 2, false, OutT>(a, stream)
+                               : launch_tm<128, 128, 2, 2, false, OutT>(a, stream);
 }
 
 }  // namespace

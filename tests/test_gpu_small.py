@@ -60,8 +60,10 @@ def test_tiny_workload_parity(path, out):
 
 # (M, H, V): ragged V, one K-step, an odd number of K-steps, the 64-row
 # boundary, ragged M past it, V = 1.
+# (100, 64, 65601): wide enough that the tiled kernel takes 160-column tiles,
+# the last of them one column wide.
 SHAPES = [(1, 32, 1), (3, 32, 17), (5, 96, 1000), (16, 64, 4111), (63, 160, 333), (64, 128, 257),
-          (65, 96, 129), (130, 224, 515), (200, 32, 2000), (7, 1024, 4097)]
+          (65, 96, 129), (130, 224, 515), (200, 32, 2000), (7, 1024, 4097), (100, 64, 65601)]
 
 
 @pytest.mark.parametrize("M,H,V", SHAPES)
