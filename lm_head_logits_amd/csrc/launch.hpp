@@ -29,6 +29,20 @@ struct Nvfp4Args {
   uint16_t *out;           // [M, V] bf16
 };
 
+// Launches `kernel` on `stream` and returns the launch's own status (not an
+// error some earlier, unrelated HIP call left behind). The argument types are
+// taken from the kernel's parameter list.
+template <typename T>
+struct arg_of {
+  using type = T;
+};
+template <typename... P>
+hipError_t launch_kernel(void (*kernel)(P...), dim3 grid, dim3 block, hipStream_t stream,
+                         typename arg_of<P>::type... args) {
+  void *ptrs[] = {static_cast<void *>(&args)...};
+  return hipLaunchKernel(reinterpret_cast<const void *>(kernel), grid, block, ptrs, 0, stream);
+}
+
 // Compute units of the current device (queried once per device).
 int device_cus();
 

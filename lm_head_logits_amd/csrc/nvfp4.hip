@@ -151,9 +151,8 @@ hipError_t launch_generic_r(const Nvfp4Args &a, hipStream_t stream) {
   dim3 grid((unsigned)(((a.V + NV_WAVES * NV_NB * 16 - 1) / (NV_WAVES * NV_NB * 16)) *
                        ((a.M + 63) / 64)));
   dim3 block(64 * NV_WAVES);
-  hipLaunchKernelGGL((nvfp4_generic_kernel<R>), grid, block, 0, stream, a.hidden, a.M, a.H, a.codes,
-                     a.scales, a.V, a.scale, a.bias, a.out);
-  return hipGetLastError();
+  return launch_kernel(nvfp4_generic_kernel<R>, grid, block, stream, a.hidden, a.M, a.H, a.codes,
+                       a.scales, a.V, a.scale, a.bias, a.out);
 }
 
 // ---------------------------------------------------------------------------
@@ -393,9 +392,8 @@ __global__ __launch_bounds__(NS_THREADS, 1) void nvfp4_stream_kernel(
 template <int R, int NB>
 hipError_t launch_stream_nb(const Nvfp4Args &a, int64_t nvs, hipStream_t stream) {
   dim3 grid((unsigned)(nvs * ((a.M + 63) / 64)));
-  hipLaunchKernelGGL((nvfp4_stream_kernel<R, NB>), grid, dim3(NS_THREADS), 0, stream, a.hidden,
-                     a.M, a.H, a.codes, a.scales, a.V, a.scale, a.bias, a.out);
-  return hipGetLastError();
+  return launch_kernel(nvfp4_stream_kernel<R, NB>, grid, dim3(NS_THREADS), stream, a.hidden, a.M,
+                       a.H, a.codes, a.scales, a.V, a.scale, a.bias, a.out);
 }
 
 // The variant with NB = the split's blocks per wave (NB <= NBM).

@@ -203,9 +203,8 @@ __global__ __launch_bounds__(SK_THREADS, SK_WAVES >= 8 ? 1 : 2) void skinny_kern
 template <int R, int NB, typename OutT>
 hipError_t launch_nb(const Bf16Args &a, int64_t nvs, hipStream_t stream) {
   dim3 grid((unsigned)(nvs * ((a.M + 63) / 64)));
-  hipLaunchKernelGGL((skinny_kernel<R, NB, OutT>), grid, dim3(SK_THREADS), 0, stream, a.hidden,
-                     a.M, a.H, a.W, a.V, a.alpha, a.bias, static_cast<OutT *>(a.out));
-  return hipGetLastError();
+  return launch_kernel(skinny_kernel<R, NB, OutT>, grid, dim3(SK_THREADS), stream, a.hidden, a.M,
+                       a.H, a.W, a.V, a.alpha, a.bias, static_cast<OutT *>(a.out));
 }
 
 // The variant with NB = the split's blocks per wave (NB <= NBM).

@@ -253,9 +253,8 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void tiled_kernel(TiledArgs args) 
 template <int TM, int TN, int WM, int WN, bool NV, typename OutT>
 hipError_t launch_tm(const TiledArgs &a, hipStream_t stream) {
   const int64_t tiles = ((a.M + TM - 1) / TM) * ((a.V + TN - 1) / TN);
-  hipLaunchKernelGGL((tiled_kernel<TM, TN, WM, WN, NV, OutT>), dim3((unsigned)tiles),
-                     dim3(64 * WM * WN), 0, stream, a);
-  return hipGetLastError();
+  return launch_kernel(tiled_kernel<TM, TN, WM, WN, NV, OutT>, dim3((unsigned)tiles),
+                       dim3(64 * WM * WN), stream, a);
 }
 
 template <typename OutT>
