@@ -67,14 +67,33 @@ __device__ __forceinline__ int hslot(int row, int ch) {
   return row * SK_CPR + (ch ^ (row & (SK_CPR < 16 ? SK_CPR - 1 : 15)));
 }
 
-template <int R, int NB, typename OutT>
+// LDS slot of 16-byte piece `p` (of 8) of row `row` of a weight block staged
+// by direct loads: rows of 128 bytes, pieces xor-swizzled by row pair so the
+// 16 rows one MFMA operand read touches fall in distinct banks.
+__device__ __forceinline__ int wslot(int row, int p) { return row * 8 + (p ^ ((row >> 1) & 7)); }
+
+typedef __attribute__((address_space(3))) void sk_lds_void;
+
+// DMA: the weight goes to LDS by direct-to-LDS buffer loads of 8 rows x 128
+// bytes (two K-steps of 8 rows) per instruction, two stages per wave in
+// flight, and reaches the MFMA through ds_read. Otherwise each lane loads its
+// own 16 bytes of a 16-row x 64-byte K-step into registers. The direct loads
+// read each weight row 128 contiguous bytes at a time (measured 2-4% faster
+// at the decode shape) but need 4 KB of LDS per column block, so they are
+// used while the work-group's blocks fit (NB <= 2).
+template <int R, int NB, bool DMA, typename OutT>
 __global__ __launch_bounds__(SK_THREADS, SK_WAVES >= 8 ? 1 : 2) void skinny_kernel(
     const uint16_t *__restrict__ hidden, int64_t M, int64_t H, const uint16_t *__restrict__ W,
     int64_t V, float alpha, const float *__restrict__ bias, OutT *__restrict__ out) {
   constexpr int ROWS = 16 * R;
   constexpr int HPC = ROWS * SK_CPR;                           // hidden pieces per chunk
   constexpr int HL = (HPC + SK_THREADS - 1) / SK_THREADS;      // ... per thread
+  static_assert(!DMA || SK_KC == 64, "a direct-load stage is one 64-element hidden chunk");
+  constexpr int WLDS = DMA ? SK_WAVES * NB * 128 : 1;          // 16-byte slots per stage buffer
   __shared__ u32x4 hs[2][ROWS * SK_CPR];
+  // Two separately declared stage buffers, so the compiler tells the stage
+  // being loaded from the one being read (and waits for the right loads).
+  __shared__ u32x4 Wl0[WLDS], Wl1[WLDS];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -136,18 +155,18 @@ __global__ __launch_bounds__(SK_THREADS, SK_WAVES >= 8 ? 1 : 2) void skinny_kern
     for (int i = 0; i < HL; ++i) hs[buf][hsl[i]] = hreg[i];
   };
 
+  f32x4 acc[NB][R];
+#pragma unroll
+  for (int j = 0; j < NB; ++j)
+#pragma unroll
+    for (int r = 0; r < R; ++r) acc[j][r] = zero4();
+
   u32x4 wb[SK_P][NB];
   auto load_w = [&](int slot, int64_t step) {
     const uint32_t soff = (uint32_t)(step * KSTEP * 2);
 #pragma unroll
     for (int j = 0; j < NB; ++j) wb[slot][j] = load16<SK_POLICY>(wr, wvoff, soff + j * wjstride);
   };
-
-  f32x4 acc[NB][R];
-#pragma unroll
-  for (int j = 0; j < NB; ++j)
-#pragma unroll
-    for (int r = 0; r < R; ++r) acc[j][r] = zero4();
 
   // One K-step of the chain on LDS buffer `buf`, slot `slot` of the weight
   // ring; then the ring slot is refilled P steps ahead (clamped to the last
@@ -163,6 +182,78 @@ __global__ __launch_bounds__(SK_THREADS, SK_WAVES >= 8 ? 1 : 2) void skinny_kern
     const int64_t next = step + SK_P < nk ? step + SK_P : nk - 1;
     load_w(slot, next);
   };
+
+  if constexpr (DMA) {
+    // Direct-load plan (as the tiled kernel's): load h of block j fills rows
+    // 8h..8h+7 of the block's 2 KB; lane l writes slot l % 8 of row l / 8,
+    // which must hold piece (l % 8) ^ swizzle(row): the swizzle of row
+    // 8h + l/8 is (4h + l/16) & 7, so the lane offset depends on h only.
+    uint32_t lvoff[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int piece = (lane % 8) ^ ((4 * h + lane / 16) & 7);
+      lvoff[h] = (uint32_t)(((lane / 8) * H + 8 * piece) * 2);
+    }
+    const int64_t nst = (nk + 1) / 2;  // stages of two K-steps (the last may hold one)
+    auto dma_stage = [&](int64_t st, u32x4 *wl) {
+      const uint32_t soff = (uint32_t)(st * 128);
+      // The buffer was just read by this wave's ds_reads, and a direct load
+      // writes LDS on its own path, not behind them: wait until they have
+      // returned (lgkmcnt(0)) before overwriting the buffer.
+      __builtin_amdgcn_s_waitcnt(0xC07F);
+#pragma unroll
+      for (int j = 0; j < NB; ++j)
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(
+              wr, (sk_lds_void *)&wl[(wave * NB + j) * 128 + 64 * h], 16, lvoff[h],
+              soff + j * wjstride + (uint32_t)(h * 8 * H * 2), 0, 0);
+    };
+    auto kstep_dma = [&](int buf, int s, const u32x4 *wl) {
+      u32x4 a[R], b[NB];
+#pragma unroll
+      for (int r = 0; r < R; ++r) a[r] = hs[buf][hslot(16 * r + li, 4 * s + lg)];
+#pragma unroll
+      for (int j = 0; j < NB; ++j) b[j] = wl[(wave * NB + j) * 128 + wslot(li, 4 * s + lg)];
+#pragma unroll
+      for (int j = 0; j < NB; ++j)
+#pragma unroll
+        for (int r = 0; r < R; ++r) acc[j][r] = kstep(acc[j][r], a[r], b[j]);
+    };
+    // One 64-element chunk (= one stage): its two K-steps, then the stage two
+    // ahead into the buffer just read, then the hidden hand-over.
+    auto chunk = [&](int64_t c, const u32x4 *wl) {
+      const int buf = (int)(c & 1);
+      kstep_dma(buf, 0, wl);
+      kstep_dma(buf, 1, wl);
+      dma_stage(c + 2 < nst ? c + 2 : nst - 1, (u32x4 *)wl);
+      sched_fence();
+      store_hidden(buf ^ 1);
+      lds_barrier();
+      load_hidden(c + 2 < nchunks ? c + 2 : nchunks - 1);
+    };
+    load_hidden(0);
+    dma_stage(0, Wl0);
+    dma_stage(nst > 1 ? 1 : 0, Wl1);
+    store_hidden(0);
+    load_hidden(nchunks > 1 ? 1 : 0);
+    lds_barrier();
+    const int64_t nfull = nk / 2;
+    int64_t c = 0;
+    for (; c + 2 <= nfull; c += 2) {
+      chunk(c, Wl0);
+      chunk(c + 1, Wl1);
+    }
+    if (c < nfull) {
+      chunk(c, Wl0);
+      ++c;
+    }
+    if (c < nst) kstep_dma((int)(c & 1), 0, (c & 1) ? Wl1 : Wl0);  // H % 64 == 32
+    if (!active) return;
+    store_blocks<R, NB>([&](int i, int j) -> f32x4 & { return acc[j][i]; }, out, m0,
+                        M - m0 < 16 * R ? M - m0 : 16 * R, cb0 * 16, cend, V, alpha, bias);
+    return;
+  }
 
   // prologue: hidden chunk 0 in LDS, the first P weight K-steps in flight,
   // hidden chunk 1 in flight. Waves past the vocabulary end run the same
@@ -203,8 +294,9 @@ __global__ __launch_bounds__(SK_THREADS, SK_WAVES >= 8 ? 1 : 2) void skinny_kern
 template <int R, int NB, typename OutT>
 hipError_t launch_nb(const Bf16Args &a, int64_t nvs, hipStream_t stream) {
   dim3 grid((unsigned)(nvs * ((a.M + 63) / 64)));
-  return launch_kernel(skinny_kernel<R, NB, OutT>, grid, dim3(SK_THREADS), stream, a.hidden, a.M,
-                       a.H, a.W, a.V, a.alpha, a.bias, static_cast<OutT *>(a.out));
+  constexpr bool DMA = NB <= 2;
+  return launch_kernel(skinny_kernel<R, NB, DMA, OutT>, grid, dim3(SK_THREADS), stream, a.hidden,
+                       a.M, a.H, a.W, a.V, a.alpha, a.bias, static_cast<OutT *>(a.out));
 }
 
 // The variant with NB = the split's blocks per wave (NB <= NBM).
