@@ -4,12 +4,14 @@
 // HBM (the sglang digest's motivation section: the fp32 head's cost was weight
 // traffic, which the bf16 x bf16 -> fp32 path cuts to one read of the bf16
 // weight). Each wave owns NB column blocks of 16 vocabulary rows and walks the
-// full H for them: every lane loads 16 contiguous bytes of one weight row per
-// K-step straight into the MFMA B operand, P K-steps ahead of their use. The
-// hidden rows (<= 64) are staged through LDS in KC-element K chunks,
-// double-buffered, so the waves of a work-group read them from L2 once. The
-// K-step chain is the one of kstep.hpp, so the results equal the tiled GEMM's
-// bit for bit.
+// full H for them, its weight loads running ahead of their use: by
+// direct-to-LDS loads of 8 rows x 128 bytes, two stages of two K-steps in
+// flight, when the work-group's blocks fit in LDS (NB <= 2); else by register
+// loads of 16 bytes per lane and K-step straight into the MFMA B operand,
+// P K-steps ahead. The hidden rows (<= 64) are staged through LDS in
+// KC-element K chunks, double-buffered, so the waves of a work-group read
+// them from L2 once. The K-step chain is the one of kstep.hpp, so the results
+// equal the tiled GEMM's bit for bit.
 //
 // Measured on MI355X (HBM read of the 1.05 GB decode weight): the order in
 // which the GPU as a whole walks the weight decides the bandwidth. Waves that
@@ -209,7 +211,21 @@ __global__ __launch_bounds__(SK_THREADS, SK_WAVES >= 8 ? 1 : 2) void skinny_kern
               wr, (sk_lds_void *)&wl[(wave * NB + j) * 128 + 64 * h], 16, lvoff[h],
               soff + j * wjstride + (uint32_t)(h * 8 * H * 2), 0, 0);
     };
+    // Before the first read of a stage buffer: wait for its direct loads.
+    // Issued after them, at most the other buffer's loads (2 NB) and one
+    // hidden chunk's loads (HL) may still be in flight. The compiler's own
+    // wait placement once let a read of the second block slip ahead of its
+    // load (single-chunk path, NB = 2), so the wait is explicit, fenced.
+    constexpr int VM_AFTER = 2 * NB + HL;
+    static_assert(VM_AFTER < 64, "vmcnt field");
+    constexpr int VM_WAIT = (VM_AFTER & 15) | ((VM_AFTER >> 4) << 14) | 0x70 | 0xF00;
+    auto wait_stage = [&]() {
+      sched_fence();
+      __builtin_amdgcn_s_waitcnt(VM_WAIT);
+      sched_fence();
+    };
     auto kstep_dma = [&](int buf, int s, const u32x4 *wl) {
+      if (s == 0) wait_stage();
       u32x4 a[R], b[NB];
 #pragma unroll
       for (int r = 0; r < R; ++r) a[r] = hs[buf][hslot(16 * r + li, 4 * s + lg)];

@@ -163,6 +163,44 @@ def test_run_to_run_identical():
         assert torch.equal(a.view(torch.int32), b.view(torch.int32))
 
 
+def test_concurrent_calls_on_several_streams_and_threads():
+    # The library keeps no per-call state: calls from several host threads,
+    # each on its own stream, give the same bits as the calls made one by one.
+    import threading
+    rng = np.random.default_rng(3)
+    say("threads and streams")
+    hd = bf16_dev(_rand_bf16(rng, (64, 256), 1.0))
+    Wd = bf16_dev(_rand_bf16(rng, (7000, 256), 0.02))
+    Ms = [1, 5, 17, 64, 40, 3, 64, 33]
+    serial = [L.logits(hd[:m], Wd, 0.25, None, path=("skinny" if i % 2 else "tiled"))
+              for i, m in enumerate(Ms)]
+    torch.cuda.synchronize()
+    outs = [None] * len(Ms)
+    errors = []
+
+    def work(i):
+        try:
+            s = torch.cuda.Stream(device=DEV)
+            with torch.cuda.stream(s):
+                o = torch.empty((Ms[i], 7000), device=DEV, dtype=torch.float32)
+                for _ in range(3):
+                    L.logits(hd[:Ms[i]], Wd, 0.25, None, out=o,
+                             path=("skinny" if i % 2 else "tiled"), stream=s)
+            s.synchronize()
+            outs[i] = o
+        except Exception as e:  # reported below, on the test's thread
+            errors.append(e)
+
+    threads = [threading.Thread(target=work, args=(i,)) for i in range(len(Ms))]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    assert not errors, errors
+    for a, b in zip(serial, outs):
+        assert torch.equal(a.view(torch.int32), b.view(torch.int32))
+
+
 # ----------------------------------------------------------------------------
 # NVFP4
 # ----------------------------------------------------------------------------
