@@ -84,6 +84,22 @@ def test_ragged_shapes_parity_and_paths_agree(M, H, V):
     assert np.array_equal(host_bits(auto), host_bits(outs["skinny"]))
 
 
+# V = 70001: more column blocks than waves on a 256-CU part, so the
+# weight-streaming kernel runs its direct-to-LDS path with two blocks per wave;
+# H covers even and odd numbers of 64-element chunks and a final half chunk.
+@pytest.mark.parametrize("H", [32, 64, 96, 160, 192, 320])
+@pytest.mark.parametrize("M", [1, 20, 64])
+def test_weight_stream_paths_match_tiled(M, H):
+    rng = np.random.default_rng(M * 7 + H)
+    V = 70001
+    say(f"stream vs tiled M={M} H={H} V={V}")
+    hd = bf16_dev(_rand_bf16(rng, (M, H), 1.0))
+    Wd = bf16_dev(_rand_bf16(rng, (V, H), 0.02))
+    a = L.logits(hd, Wd, 0.5, None, torch.float32, path="skinny")
+    b = L.logits(hd, Wd, 0.5, None, torch.float32, path="tiled")
+    assert torch.equal(a.view(torch.int32), b.view(torch.int32))
+
+
 def test_integer_inputs_are_exact_small():
     # |partial sums| <= 16 * H < 2^24: every summation order is exact, so the
     # GPU must equal the oracle bit for bit.
