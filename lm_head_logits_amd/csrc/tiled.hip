@@ -7,13 +7,14 @@
 // folded into the epilogue (section "muP is folded into the fp32 GEMM").
 //
 // Work-group tile 256 x 256 output elements with eight waves in a 4 x 2
-// arrangement (64 x 128 per wave), or 128 x 128 / 128 x 160 with four waves of
-// 64 x 64 / 64 x 80 when M <= 128. Each wave's 16 x 16 MFMA blocks keep their fp32 accumulators in
-// registers for the whole K loop. K is staged through LDS 64 elements at a
-// time, double-buffered:
-// the loads of stage k+1 are issued as direct-to-LDS buffer loads
-// (buffer_load_dwordx4 ... lds, no registers) before the MFMAs of stage k run,
-// and one barrier per stage hands the buffers over. Every output element is
+// arrangement (64 x 128 per wave), or 128 x 128 / 128 x 160 with four waves
+// of 64 x 64 / 64 x 80 when M <= 128. Each wave's 16 x 16 MFMA blocks keep
+// their fp32 accumulators in registers for the whole K loop. K is staged
+// through LDS 64 elements at a time, double-buffered: the loads of stage k+1
+// are issued as direct-to-LDS buffer loads (buffer_load_dwordx4 ... lds, no
+// registers) before the MFMAs of stage k run, and one barrier per stage
+// (which also waits for those loads) hands the buffers over. Every output
+// element is
 // built by the K-step chain of kstep.hpp -- ascending K, one accumulator, the
 // same operand map -- so a row's bits equal the weight-streaming kernel's and
 // do not depend on M.
