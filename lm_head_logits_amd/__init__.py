@@ -65,6 +65,11 @@ def _need(cond: bool, msg: str):
         raise ValueError(msg)
 
 
+def _same_device(*tensors):
+    devs = {t.device for t in tensors if t is not None}
+    _need(len(devs) == 1, f"all tensors must be on one device, got {sorted(map(str, devs))}")
+
+
 _PATHS = {"auto": PATH_AUTO, "skinny": PATH_SKINNY, "tiled": PATH_TILED}
 
 
@@ -90,11 +95,13 @@ def logits(hidden: torch.Tensor, weight: torch.Tensor, alpha: float = 1.0, bias=
     else:
         _need(out.is_cuda and out.dtype == out_dtype and out.shape == (M, V) and out.is_contiguous(),
               "out must be a contiguous [M, V] device tensor of out_dtype")
-    st = _lib.load().lmhead_logits_path(
-        hidden.data_ptr(), M, H, weight.data_ptr(), V, float(alpha),
-        bias.data_ptr() if bias is not None else None,
-        LMHEAD_BF16 if out_dtype == torch.bfloat16 else LMHEAD_F32,
-        out.data_ptr(), _stream_handle(hidden.device, stream), _PATHS[path])
+    _same_device(hidden, weight, bias, out)
+    with torch.cuda.device(hidden.device):  # the library launches on the current device
+        st = _lib.load().lmhead_logits_path(
+            hidden.data_ptr(), M, H, weight.data_ptr(), V, float(alpha),
+            bias.data_ptr() if bias is not None else None,
+            LMHEAD_BF16 if out_dtype == torch.bfloat16 else LMHEAD_F32,
+            out.data_ptr(), _stream_handle(hidden.device, stream), _PATHS[path])
     _check(st, "lmhead_logits")
     return out
 
@@ -122,10 +129,12 @@ def logits_nvfp4(hidden: torch.Tensor, codes: torch.Tensor, scales: torch.Tensor
     else:
         _need(out.is_cuda and out.dtype == torch.bfloat16 and out.shape == (M, V)
               and out.is_contiguous(), "out must be a contiguous bf16 [M, V] device tensor")
-    st = _lib.load().lmhead_logits_nvfp4(
-        hidden.data_ptr(), M, H, codes.data_ptr(), scales.data_ptr(), float(global_scale), V,
-        float(alpha), bias.data_ptr() if bias is not None else None, out.data_ptr(),
-        _stream_handle(hidden.device, stream))
+    _same_device(hidden, codes, scales, bias, out)
+    with torch.cuda.device(hidden.device):  # the library launches on the current device
+        st = _lib.load().lmhead_logits_nvfp4(
+            hidden.data_ptr(), M, H, codes.data_ptr(), scales.data_ptr(), float(global_scale), V,
+            float(alpha), bias.data_ptr() if bias is not None else None, out.data_ptr(),
+            _stream_handle(hidden.device, stream))
     _check(st, "lmhead_logits_nvfp4")
     return out
 

@@ -6,14 +6,14 @@
 // them to E4M3 would fall below the declared precision), rows go through in
 // calls of at most 64, and a row's logits do not depend on the row count.
 //
-// Here one launch covers every 64-row block of the call (the blocks of one
-// vocabulary slice are neighbours in launch order, so a weight slice is read
-// from HBM once and re-read from cache by the other blocks). Each lane decodes
-// the 8 codes it feeds to one MFMA B operand -- e2m1 * e4m3 is exact in bf16
-// (at most 6 significant bits, exponent inside bf16's range) -- and the
-// K-step chain of kstep.hpp runs unchanged. So this kernel's logits equal
-// lmhead_logits on the dequantised weight with alpha = fl32(g * alpha), bit
-// for bit.
+// Here a call of up to 64 rows runs the weight-streaming kernels below, in
+// which each lane decodes the 8 codes it feeds to one MFMA B operand --
+// e2m1 * e4m3 is exact in bf16 (at most 6 significant bits, exponent inside
+// bf16's range) -- and the K-step chain of kstep.hpp runs unchanged. A call
+// of more rows runs the tiled kernel (tiled.hip), which decodes each weight
+// element once per 128-row tile into LDS and runs the same chain. Either way
+// the logits equal lmhead_logits on the dequantised weight with
+// alpha = fl32(g * alpha), bit for bit, so a row's bits do not depend on M.
 #include <type_traits>
 
 #include "kstep.hpp"
