@@ -6,8 +6,9 @@ V=128256, bf16 weight ~N(0, 0.02), hidden ~N(0, 1), fp32 logits, alpha=1/16):
 one lmhead_logits call for each M in {1, 2, 8, 32, 64}. The headline value is
 the whole step's algorithmic HBM throughput (weight read once + hidden +
 output written, divided by the step time). The other workloads -- prefill
-(M=2048), spec-decode (M=128 with bias) and the NVFP4 head (M in 1, 16, 64,
-256) -- are timed after it and reported alongside.
+(M=2048), spec-decode (M=128 with bias), the NVFP4 head (M in 1, 16, 64,
+256) and fp16 inputs (M in 1, 64, 2048) -- are timed after it and reported
+alongside.
 
 Inputs are generated on the host from the seeded generator, copied to HBM
 before timing, and never touched by the timed region. Timing uses HIP events
@@ -205,6 +206,36 @@ def bench_nvfp4(torch, L, wl, dev, warmup, steps, copies=4):
     return res
 
 
+def bench_f16(torch, L, wl, dev, warmup, steps):
+    """fp16 hidden and weight, fp32 logits: decode rows (HBM-bound) and one
+    prefill batch (MFMA-bound) over the same [V, H] head."""
+    w = wl.F16
+    log("f16: generating inputs")
+    h, W = wl.hidden(w), wl.weight(w)
+    hd = torch.from_numpy(h.view(np.int16)).view(torch.float16).to(dev)
+    Wd = torch.from_numpy(W.view(np.int16)).view(torch.float16).to(dev)
+    alpha = w.alphas[0]
+    res = {}
+    for M in w.Ms:
+        out = torch.empty((M, w.V), dtype=torch.float32, device=dev)
+        n = steps if M <= 64 else max(5, steps // 5)
+        _, _, per = timed_calls(torch, [lambda: L.logits(hd[:M], Wd, alpha, None, out=out)],
+                                warmup, n)
+        us = 1e3 * float(np.mean(per[0]))
+        by = bytes_bf16(M, w.H, w.V, 4, False)       # fp16 elements are 2 bytes, as bf16
+        f = flops(M, w.H, w.V)
+        r = {"us_avg": round(us, 2), "GBps": round(by / us / 1e3, 1),
+             "TFLOPs": round(f / us / 1e6, 1)}
+        if M <= 64:
+            r["frac_hbm"] = round(by / us / 1e3 / HBM_PEAK_GBPS, 4)
+        else:
+            r["frac_mfma"] = round(f / us / 1e6 / BF16_PEAK_TFLOPS, 4)   # fp16 peak = bf16 peak
+        res[str(M)] = r
+        del out
+    del hd, Wd
+    return res
+
+
 def bench_copy(torch, dev, warmup, steps, nbytes=1 << 30):
     """A plain device-to-device copy of `nbytes` (torch's copy kernel): reads
     and writes exactly nbytes, so the HBM counters read on it give the scale
@@ -259,7 +290,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--only", choices=["decode", "prefill", "spec", "nvfp4", "copy", "all"], default="all",
+    ap.add_argument("--only", choices=["decode", "prefill", "spec", "nvfp4", "f16", "copy", "all"],
+                    default="all",
                     help="run one workload only (for profiling; 'copy' is the HBM counter "
                          "calibration); the headline line needs decode")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -282,6 +314,7 @@ def main():
         fn = {"prefill": lambda: bench_prefill(torch, L, wl, dev, args.warmup, args.steps),
               "spec": lambda: bench_spec(torch, L, wl, dev, args.warmup, args.steps),
               "nvfp4": lambda: bench_nvfp4(torch, L, wl, dev, args.warmup, args.steps),
+              "f16": lambda: bench_f16(torch, L, wl, dev, args.warmup, args.steps),
               "copy": lambda: bench_copy(torch, dev, args.warmup, args.steps)}[args.only]
         print(json.dumps({"workload": args.only, "result": fn()}), flush=True)
         return
@@ -294,6 +327,9 @@ def main():
         torch.cuda.empty_cache()
     if run("nvfp4"):
         extra["nvfp4"] = bench_nvfp4(torch, L, wl, dev, args.warmup, args.steps)
+        torch.cuda.empty_cache()
+    if run("f16"):
+        extra["f16_inputs"] = bench_f16(torch, L, wl, dev, args.warmup, args.steps)
 
     w = dec["w"]
     step_ms = dec["step_ms"]

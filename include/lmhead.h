@@ -53,14 +53,15 @@ extern "C" {
 #endif
 
 typedef enum {
-  LMHEAD_F32 = 0,  /* fp32 logits, 4 bytes per element */
-  LMHEAD_BF16 = 1  /* bf16 logits (round to nearest even), 2 bytes per element */
+  LMHEAD_F32 = 0,   /* fp32, 4 bytes per element */
+  LMHEAD_BF16 = 1,  /* bf16, 2 bytes per element (logits: rounded to nearest even) */
+  LMHEAD_F16 = 2    /* IEEE fp16, 2 bytes per element (logits: rounded to nearest even) */
 } lmhead_dtype;
 
 typedef enum {
   LMHEAD_OK = 0,           /* work enqueued on `stream`, or M == 0 and nothing to do */
-  LMHEAD_NOT_HANDLED = 1,  /* well-formed, outside the shape contract: nothing launched,
-                              the caller falls back */
+  LMHEAD_NOT_HANDLED = 1,  /* well-formed, outside the shape or dtype contract: nothing
+                              launched, the caller falls back */
   LMHEAD_ERR_INVALID = -1, /* NULL pointer with M > 0, M < 0, H <= 0, V <= 0, unknown dtype
                               or path, sizes beyond the documented maxima */
   LMHEAD_ERR_ALIGN = -2,   /* a base pointer below its required alignment */
@@ -108,6 +109,23 @@ lmhead_status lmhead_logits(const void *hidden, int64_t M, int64_t H, const void
 lmhead_status lmhead_logits_path(const void *hidden, int64_t M, int64_t H, const void *W,
                                  int64_t V, float alpha, const float *bias,
                                  lmhead_dtype out_dtype, void *out, void *stream, int path);
+
+/* The projection with 16-bit inputs of either kind: hidden and W both bf16,
+ * or both IEEE fp16 (sglang PR 32370 digest, implementation breakdown and the
+ * key source excerpt: the fp32-output fast path takes bf16 or fp16 inputs of
+ * one dtype and falls back otherwise). fp16 inputs run the fp16 MFMA of the
+ * same shape through the same K-step chain and epilogue, so everything said
+ * of lmhead_logits holds with fp16 in place of bf16.
+ *   in_dtype   LMHEAD_BF16 or LMHEAD_F16: the type of hidden and of W
+ *   out_dtype  LMHEAD_F32, or in_dtype (logits rounded to nearest even)
+ *   path       as in lmhead_logits_path
+ * Returns LMHEAD_NOT_HANDLED for any other (in_dtype, out_dtype) pair, for
+ * instance fp32 inputs (nothing launched; the caller falls back), else as
+ * lmhead_logits. lmhead_logits(...) is lmhead_logits_ex(..., LMHEAD_BF16,
+ * out_dtype, out, stream, LMHEAD_PATH_AUTO). */
+lmhead_status lmhead_logits_ex(const void *hidden, int64_t M, int64_t H, const void *W, int64_t V,
+                               float alpha, const float *bias, lmhead_dtype in_dtype,
+                               lmhead_dtype out_dtype, void *out, void *stream, int path);
 
 /* The NVFP4 W4A16 head (bf16 logits).
  *   hidden       bf16 [M, H]                    (device, read)

@@ -13,8 +13,8 @@ from __future__ import annotations
 import torch
 
 from . import _lib
-from ._lib import (LMHEAD_BF16, LMHEAD_F32, NOT_HANDLED, OK, PATH_AUTO, PATH_NONE, PATH_NVFP4,
-                   PATH_SKINNY, PATH_TILED)
+from ._lib import (LMHEAD_BF16, LMHEAD_F16, LMHEAD_F32, NOT_HANDLED, OK, PATH_AUTO, PATH_NONE,
+                   PATH_NVFP4, PATH_SKINNY, PATH_TILED)
 
 __all__ = ["logits", "logits_nvfp4", "shape_ok", "path_for", "status_string", "version",
            "LmHeadError", "NotHandled", "PATH_SKINNY", "PATH_TILED", "PATH_NVFP4", "PATH_AUTO",
@@ -73,20 +73,25 @@ def _same_device(*tensors):
 _PATHS = {"auto": PATH_AUTO, "skinny": PATH_SKINNY, "tiled": PATH_TILED}
 
 
+_DTYPES = {torch.float32: LMHEAD_F32, torch.bfloat16: LMHEAD_BF16, torch.float16: LMHEAD_F16}
+
+
 def logits(hidden: torch.Tensor, weight: torch.Tensor, alpha: float = 1.0, bias=None,
            out_dtype=torch.float32, out: torch.Tensor | None = None, *, path: str = "auto",
            stream=None) -> torch.Tensor:
-    """alpha * hidden @ weight.T (+ bias): bf16 [M, H] x bf16 [V, H] -> [M, V]
-    fp32 or bf16, accumulated at fp32 (lmhead_logits / lmhead_logits_path)."""
+    """alpha * hidden @ weight.T (+ bias): [M, H] x [V, H] -> [M, V], both inputs
+    bf16 or both fp16, accumulated at fp32, logits fp32 or of the input type
+    (lmhead_logits_ex). Other dtype combinations raise NotHandled (nothing
+    runs; the caller falls back)."""
     _need(hidden.is_cuda and weight.is_cuda, "hidden and weight must be device tensors")
-    _need(hidden.dtype == torch.bfloat16 and weight.dtype == torch.bfloat16,
-          "hidden and weight must be bf16")
+    _need(hidden.dtype in _DTYPES and weight.dtype in _DTYPES and out_dtype in _DTYPES,
+          "dtypes must be float32, bfloat16 or float16")
     _need(hidden.dim() == 2 and weight.dim() == 2, "hidden [M, H] and weight [V, H] are 2-D")
     _need(hidden.is_contiguous() and weight.is_contiguous(), "inputs must be contiguous")
     M, H = hidden.shape
     V, H2 = weight.shape
     _need(H == H2, f"hidden has H={H}, weight has H={H2}")
-    _need(out_dtype in (torch.float32, torch.bfloat16), "out_dtype is float32 or bfloat16")
+    in_code = _DTYPES[hidden.dtype] if hidden.dtype == weight.dtype else LMHEAD_F32
     if bias is not None:
         _need(bias.is_cuda and bias.dtype == torch.float32 and bias.shape == (V,)
               and bias.is_contiguous(), "bias must be a contiguous fp32 device tensor [V]")
@@ -97,12 +102,11 @@ def logits(hidden: torch.Tensor, weight: torch.Tensor, alpha: float = 1.0, bias=
               "out must be a contiguous [M, V] device tensor of out_dtype")
     _same_device(hidden, weight, bias, out)
     with torch.cuda.device(hidden.device):  # the library launches on the current device
-        st = _lib.load().lmhead_logits_path(
+        st = _lib.load().lmhead_logits_ex(
             hidden.data_ptr(), M, H, weight.data_ptr(), V, float(alpha),
-            bias.data_ptr() if bias is not None else None,
-            LMHEAD_BF16 if out_dtype == torch.bfloat16 else LMHEAD_F32,
+            bias.data_ptr() if bias is not None else None, in_code, _DTYPES[out_dtype],
             out.data_ptr(), _stream_handle(hidden.device, stream), _PATHS[path])
-    _check(st, "lmhead_logits")
+    _check(st, "lmhead_logits_ex")
     return out
 
 

@@ -12,6 +12,7 @@ from . import _build
 
 LMHEAD_F32 = 0
 LMHEAD_BF16 = 1
+LMHEAD_F16 = 2
 
 OK = 0
 NOT_HANDLED = 1
@@ -25,8 +26,8 @@ PATH_SKINNY = 0
 PATH_TILED = 1
 PATH_NVFP4 = 2
 
-EXPORTS = ("lmhead_logits", "lmhead_logits_path", "lmhead_logits_nvfp4", "lmhead_shape_ok",
-           "lmhead_path_for", "lmhead_status_string", "lmhead_version")
+EXPORTS = ("lmhead_logits", "lmhead_logits_path", "lmhead_logits_ex", "lmhead_logits_nvfp4",
+           "lmhead_shape_ok", "lmhead_path_for", "lmhead_status_string", "lmhead_version")
 
 _lib = None
 
@@ -48,6 +49,8 @@ def load() -> ctypes.CDLL:
     lib.lmhead_logits.argtypes = [vp, i64, i64, vp, i64, f32, vp, i32, vp, vp]
     lib.lmhead_logits_path.restype = i32
     lib.lmhead_logits_path.argtypes = [vp, i64, i64, vp, i64, f32, vp, i32, vp, vp, i32]
+    lib.lmhead_logits_ex.restype = i32
+    lib.lmhead_logits_ex.argtypes = [vp, i64, i64, vp, i64, f32, vp, i32, i32, vp, vp, i32]
     lib.lmhead_logits_nvfp4.restype = i32
     lib.lmhead_logits_nvfp4.argtypes = [vp, i64, i64, vp, vp, f32, i64, f32, vp, vp, vp]
     lib.lmhead_shape_ok.restype = i32

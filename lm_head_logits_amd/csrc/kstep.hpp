@@ -32,16 +32,24 @@
 namespace lmhead {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int KSTEP = 32;  // K consumed by one MFMA
 
-// One step of the chain: acc += A(16 x 32) * B(32 x 16), bf16 in, fp32 out.
+// One step of the chain: acc += A(16 x 32) * B(32 x 16), fp32 out; bf16
+// inputs, or fp16 inputs (F16) through the fp16 MFMA of the same shape and
+// operand map.
+template <bool F16 = false>
 __device__ __forceinline__ f32x4 kstep(f32x4 acc, u32x4 a, u32x4 b) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
-                                                 __builtin_bit_cast(bf16x8, b), acc, 0, 0, 0);
+  if constexpr (F16)
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
+                                                  __builtin_bit_cast(f16x8, b), acc, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), acc, 0, 0, 0);
 }
 
 __device__ __forceinline__ f32x4 zero4() { return f32x4{0.0f, 0.0f, 0.0f, 0.0f}; }
@@ -129,8 +137,9 @@ __device__ __forceinline__ float epilogue_v(float acc, float alpha, bool has_bia
   return t;
 }
 
-// One output element through a buffer resource: fp32, or bf16 rounded to
-// nearest even. Offsets past the resource are dropped by the hardware.
+// One output element through a buffer resource: fp32, or bf16 / fp16
+// rounded to nearest even. Offsets past the resource are dropped by the
+// hardware.
 template <typename OutT>
 __device__ __forceinline__ void store_c(rsrc_t r, uint32_t voff, uint32_t soff, float t);
 
@@ -149,6 +158,13 @@ __device__ __forceinline__ void store_c<float>(rsrc_t r, uint32_t voff, uint32_t
 template <>
 __device__ __forceinline__ void store_c<uint16_t>(rsrc_t r, uint32_t voff, uint32_t soff, float t) {
   __builtin_amdgcn_raw_buffer_store_b16(bf16_rne(t), r, voff, soff, STORE_POLICY);
+}
+
+// fp16 logits: the conversion rounds to nearest even (the default mode).
+template <>
+__device__ __forceinline__ void store_c<_Float16>(rsrc_t r, uint32_t voff, uint32_t soff, float t) {
+  __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(uint16_t, (_Float16)t), r, voff, soff,
+                                        STORE_POLICY);
 }
 
 // An offset past any output resource (resources are < 1 GiB and scalar

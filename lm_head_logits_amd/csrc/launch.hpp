@@ -7,14 +7,18 @@
 
 namespace lmhead {
 
-struct Bf16Args {
-  const uint16_t *hidden;  // [M, H] bf16
+// Element type of the logits.
+enum OutType { OUT_F32 = 0, OUT_BF16 = 1, OUT_F16 = 2 };
+
+struct GemmArgs {
+  const uint16_t *hidden;  // [M, H] bf16, or fp16 when in_f16
   int64_t M, H;
-  const uint16_t *W;       // [V, H] bf16
+  const uint16_t *W;       // [V, H] of the same type as hidden
   int64_t V;
   float alpha;
   const float *bias;       // [V] or nullptr
-  int out_bf16;            // 0: fp32 out, 1: bf16 out
+  int in_f16;              // 0: bf16 inputs, 1: fp16 inputs
+  OutType out_type;        // OUT_F32, or the input type
   void *out;               // [M, V]
 };
 
@@ -60,8 +64,8 @@ struct VSplit {
 };
 VSplit vsplit(int64_t ncb, int waves, int nb_max);
 
-hipError_t launch_skinny(const Bf16Args &a, hipStream_t stream);
-hipError_t launch_tiled(const Bf16Args &a, hipStream_t stream);
+hipError_t launch_skinny(const GemmArgs &a, hipStream_t stream);
+hipError_t launch_tiled(const GemmArgs &a, hipStream_t stream);
 hipError_t launch_nvfp4(const Nvfp4Args &a, hipStream_t stream);
 hipError_t launch_tiled_nvfp4(const Nvfp4Args &a, hipStream_t stream);
 

@@ -30,6 +30,8 @@ lmhead_status check_shape(int64_t M, int64_t H, int64_t V) {
 
 int auto_path(int64_t M) { return M <= 64 ? LMHEAD_PATH_SKINNY : LMHEAD_PATH_TILED; }
 
+bool known_dtype(int d) { return d == LMHEAD_F32 || d == LMHEAD_BF16 || d == LMHEAD_F16; }
+
 }  // namespace
 
 namespace lmhead {
@@ -85,21 +87,24 @@ const char *lmhead_status_string(int status) {
 
 const char *lmhead_version(void) { return "0.1.0"; }
 
-lmhead_status lmhead_logits_path(const void *hidden, int64_t M, int64_t H, const void *W,
-                                 int64_t V, float alpha, const float *bias,
-                                 lmhead_dtype out_dtype, void *out, void *stream, int path) {
+lmhead_status lmhead_logits_ex(const void *hidden, int64_t M, int64_t H, const void *W, int64_t V,
+                               float alpha, const float *bias, lmhead_dtype in_dtype,
+                               lmhead_dtype out_dtype, void *out, void *stream, int path) {
   lmhead_status st = check_shape(M, H, V);
   if (st != LMHEAD_OK) return st;
-  if (out_dtype != LMHEAD_F32 && out_dtype != LMHEAD_BF16) return LMHEAD_ERR_INVALID;
+  if (!known_dtype(in_dtype) || !known_dtype(out_dtype)) return LMHEAD_ERR_INVALID;
   if (path != LMHEAD_PATH_AUTO && path != LMHEAD_PATH_SKINNY && path != LMHEAD_PATH_TILED)
     return LMHEAD_ERR_INVALID;
+  // 16-bit inputs of one type; logits fp32 or of the input type
+  if (in_dtype == LMHEAD_F32 || (out_dtype != LMHEAD_F32 && out_dtype != in_dtype))
+    return LMHEAD_NOT_HANDLED;
   if (M == 0) return LMHEAD_OK;  // nothing to do, nothing launched
   if (hidden == nullptr || W == nullptr || out == nullptr) return LMHEAD_ERR_INVALID;
   if (!aligned(hidden, 16) || !aligned(W, 16) || !aligned(out, 16) ||
       (bias != nullptr && !aligned(bias, 4)))
     return LMHEAD_ERR_ALIGN;
 
-  lmhead::Bf16Args a;
+  lmhead::GemmArgs a;
   a.hidden = static_cast<const uint16_t *>(hidden);
   a.M = M;
   a.H = H;
@@ -107,12 +112,27 @@ lmhead_status lmhead_logits_path(const void *hidden, int64_t M, int64_t H, const
   a.V = V;
   a.alpha = alpha;
   a.bias = bias;
-  a.out_bf16 = out_dtype == LMHEAD_BF16 ? 1 : 0;
+  a.in_f16 = in_dtype == LMHEAD_F16 ? 1 : 0;
+  a.out_type = out_dtype == LMHEAD_F32    ? lmhead::OUT_F32
+               : out_dtype == LMHEAD_BF16 ? lmhead::OUT_BF16
+                                          : lmhead::OUT_F16;
   a.out = out;
   const int p = path == LMHEAD_PATH_AUTO ? auto_path(M) : path;
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e = p == LMHEAD_PATH_SKINNY ? lmhead::launch_skinny(a, s) : lmhead::launch_tiled(a, s);
   return e == hipSuccess ? LMHEAD_OK : LMHEAD_ERR_DEVICE;
+}
+
+lmhead_status lmhead_logits_path(const void *hidden, int64_t M, int64_t H, const void *W,
+                                 int64_t V, float alpha, const float *bias,
+                                 lmhead_dtype out_dtype, void *out, void *stream, int path) {
+  // the bf16 entry points take fp32 or bf16 logits only
+  if (out_dtype != LMHEAD_F32 && out_dtype != LMHEAD_BF16) {
+    const lmhead_status st = check_shape(M, H, V);
+    return st != LMHEAD_OK ? st : LMHEAD_ERR_INVALID;
+  }
+  return lmhead_logits_ex(hidden, M, H, W, V, alpha, bias, LMHEAD_BF16, out_dtype, out, stream,
+                          path);
 }
 
 lmhead_status lmhead_logits(const void *hidden, int64_t M, int64_t H, const void *W, int64_t V,

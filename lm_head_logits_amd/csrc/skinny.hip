@@ -83,7 +83,7 @@ typedef __attribute__((address_space(3))) void sk_lds_void;
 // read each weight row 128 contiguous bytes at a time (measured 2-4% faster
 // at the decode shape) but need 4 KB of LDS per column block, so they are
 // used while the work-group's blocks fit (NB <= 2).
-template <int R, int NB, bool DMA, typename OutT>
+template <int R, int NB, bool DMA, bool F16, typename OutT>
 __global__ __launch_bounds__(SK_THREADS, SK_WAVES >= 8 ? 1 : 2) void skinny_kernel(
     const uint16_t *__restrict__ hidden, int64_t M, int64_t H, const uint16_t *__restrict__ W,
     int64_t V, float alpha, const float *__restrict__ bias, OutT *__restrict__ out) {
@@ -180,7 +180,7 @@ __global__ __launch_bounds__(SK_THREADS, SK_WAVES >= 8 ? 1 : 2) void skinny_kern
 #pragma unroll
     for (int j = 0; j < NB; ++j)
 #pragma unroll
-      for (int r = 0; r < R; ++r) acc[j][r] = kstep(acc[j][r], a[r], wb[slot][j]);
+      for (int r = 0; r < R; ++r) acc[j][r] = kstep<F16>(acc[j][r], a[r], wb[slot][j]);
     const int64_t next = step + SK_P < nk ? step + SK_P : nk - 1;
     load_w(slot, next);
   };
@@ -234,7 +234,7 @@ __global__ __launch_bounds__(SK_THREADS, SK_WAVES >= 8 ? 1 : 2) void skinny_kern
 #pragma unroll
       for (int j = 0; j < NB; ++j)
 #pragma unroll
-        for (int r = 0; r < R; ++r) acc[j][r] = kstep(acc[j][r], a[r], b[j]);
+        for (int r = 0; r < R; ++r) acc[j][r] = kstep<F16>(acc[j][r], a[r], b[j]);
     };
     // One 64-element chunk (= one stage): its two K-steps, then the stage two
     // ahead into the buffer just read, then the hidden hand-over.
@@ -307,45 +307,49 @@ __global__ __launch_bounds__(SK_THREADS, SK_WAVES >= 8 ? 1 : 2) void skinny_kern
                       M - m0 < 16 * R ? M - m0 : 16 * R, cb0 * 16, cend, V, alpha, bias);
 }
 
-template <int R, int NB, typename OutT>
-hipError_t launch_nb(const Bf16Args &a, int64_t nvs, hipStream_t stream) {
+template <int R, int NB, bool F16, typename OutT>
+hipError_t launch_nb(const GemmArgs &a, int64_t nvs, hipStream_t stream) {
   dim3 grid((unsigned)(nvs * ((a.M + 63) / 64)));
   constexpr bool DMA = NB <= 2;
-  return launch_kernel(skinny_kernel<R, NB, DMA, OutT>, grid, dim3(SK_THREADS), stream, a.hidden,
-                       a.M, a.H, a.W, a.V, a.alpha, a.bias, static_cast<OutT *>(a.out));
+  return launch_kernel(skinny_kernel<R, NB, DMA, F16, OutT>, grid, dim3(SK_THREADS), stream,
+                       a.hidden, a.M, a.H, a.W, a.V, a.alpha, a.bias, static_cast<OutT *>(a.out));
 }
 
 // The variant with NB = the split's blocks per wave (NB <= NBM).
-template <int R, int NBM, typename OutT>
-hipError_t launch_split(const Bf16Args &a, const VSplit &sp, hipStream_t stream) {
+template <int R, int NBM, bool F16, typename OutT>
+hipError_t launch_split(const GemmArgs &a, const VSplit &sp, hipStream_t stream) {
   if constexpr (NBM > 1) {
-    if (sp.nb < NBM) return launch_split<R, NBM - 1, OutT>(a, sp, stream);
+    if (sp.nb < NBM) return launch_split<R, NBM - 1, F16, OutT>(a, sp, stream);
   }
-  return launch_nb<R, NBM, OutT>(a, sp.nvs, stream);
+  return launch_nb<R, NBM, F16, OutT>(a, sp.nvs, stream);
 }
 
-template <int R, typename OutT>
-hipError_t launch_r(const Bf16Args &a, hipStream_t stream) {
+template <int R, bool F16, typename OutT>
+hipError_t launch_r(const GemmArgs &a, hipStream_t stream) {
   constexpr int NBM = sk_nb_max<R>();
-  return launch_split<R, NBM, OutT>(a, vsplit((a.V + 15) / 16, SK_WAVES, NBM), stream);
+  return launch_split<R, NBM, F16, OutT>(a, vsplit((a.V + 15) / 16, SK_WAVES, NBM), stream);
 }
 
-template <typename OutT>
-hipError_t launch_t(const Bf16Args &a, hipStream_t stream) {
+template <bool F16, typename OutT>
+hipError_t launch_t(const GemmArgs &a, hipStream_t stream) {
   // Row blocks per 64-row chunk: only as many as the rows present need.
   const int64_t rows = a.M < 64 ? a.M : 64;
   switch ((rows + 15) / 16) {
-    case 1: return launch_r<1, OutT>(a, stream);
-    case 2: return launch_r<2, OutT>(a, stream);
-    case 3: return launch_r<3, OutT>(a, stream);
-    default: return launch_r<4, OutT>(a, stream);
+    case 1: return launch_r<1, F16, OutT>(a, stream);
+    case 2: return launch_r<2, F16, OutT>(a, stream);
+    case 3: return launch_r<3, F16, OutT>(a, stream);
+    default: return launch_r<4, F16, OutT>(a, stream);
   }
 }
 
 }  // namespace
 
-hipError_t launch_skinny(const Bf16Args &a, hipStream_t stream) {
-  return a.out_bf16 ? launch_t<uint16_t>(a, stream) : launch_t<float>(a, stream);
+hipError_t launch_skinny(const GemmArgs &a, hipStream_t stream) {
+  if (a.in_f16)
+    return a.out_type == OUT_F32 ? launch_t<true, float>(a, stream)
+                                 : launch_t<true, _Float16>(a, stream);
+  return a.out_type == OUT_F32 ? launch_t<false, float>(a, stream)
+                               : launch_t<false, uint16_t>(a, stream);
 }
 
 }  // namespace lmhead

@@ -53,12 +53,13 @@ __device__ __forceinline__ void dma16(rsrc_t r, void *dst, uint32_t voff, uint32
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)dst, 16, voff, soff, 0, 0);
 }
 
-// Arguments of one tiled launch. The B operand is either a bf16 weight (W)
-// or an NVFP4 weight (codes, scales) decoded on its way into LDS.
+// Arguments of one tiled launch. The B operand is either a 16-bit weight W
+// (bf16, or fp16 with fp16 hidden) or an NVFP4 weight (codes, scales)
+// decoded on its way into LDS.
 struct TiledArgs {
-  const uint16_t *hidden;  // [M, H] bf16
+  const uint16_t *hidden;  // [M, H] bf16 or fp16
   int64_t M, H;
-  const uint16_t *W;       // [V, H] bf16 (bf16 weight)
+  const uint16_t *W;       // [V, H] bf16 or fp16 (16-bit weight)
   const uint8_t *codes;    // [V, H/2] E2M1 pairs (NVFP4 weight)
   const uint8_t *scales;   // [V, H/16] E4M3 (NVFP4 weight)
   int64_t V;
@@ -76,7 +77,7 @@ struct TiledArgs {
 // loads it one stage ahead into registers, and at the stage's turn decodes it
 // (exact bf16, nvfp4_decode.hpp) into the same swizzled LDS layout the direct
 // loads fill. Every weight element is decoded once per tile, whatever M.
-template <int TM, int TN, int WM, int WN, bool NV, typename OutT>
+template <int TM, int TN, int WM, int WN, bool NV, bool F16, typename OutT>
 __global__ __launch_bounds__(64 * WM * WN, 1) void tiled_kernel(TiledArgs args) {
   const uint16_t *__restrict__ hidden = args.hidden;
   const int64_t M = args.M, H = args.H, V = args.V;
@@ -210,7 +211,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void tiled_kernel(TiledArgs args) 
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
-      for (int j = 0; j < FN; ++j) acc[i][j] = kstep(acc[i][j], a[i], bb[j]);
+      for (int j = 0; j < FN; ++j) acc[i][j] = kstep<F16>(acc[i][j], a[i], bb[j]);
   };
 
   // Stages alternate between the two buffers; the loop body covers two stages
@@ -251,16 +252,16 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void tiled_kernel(TiledArgs args) 
                        M - rb < SM ? M - rb : SM, n0 + wn * SN, V, V, alpha, bias);
 }
 
-template <int TM, int TN, int WM, int WN, bool NV, typename OutT>
+template <int TM, int TN, int WM, int WN, bool NV, bool F16, typename OutT>
 hipError_t launch_tm(const TiledArgs &a, hipStream_t stream) {
   const int64_t tiles = ((a.M + TM - 1) / TM) * ((a.V + TN - 1) / TN);
-  return launch_kernel(tiled_kernel<TM, TN, WM, WN, NV, OutT>, dim3((unsigned)tiles),
+  return launch_kernel(tiled_kernel<TM, TN, WM, WN, NV, F16, OutT>, dim3((unsigned)tiles),
                        dim3(64 * WM * WN), stream, a);
 }
 
-template <typename OutT>
+template <bool F16, typename OutT>
 hipError_t launch_t(const TiledArgs &a, hipStream_t stream) {
-  if (a.M > 128) return launch_tm<256, 256, 4, 2, false, OutT>(a, stream);
+  if (a.M > 128) return launch_tm<256, 256, 4, 2, false, F16, OutT>(a, stream);
   // M <= 128: one 128-row tile covers M; four waves (2 x 2), two tiles
   // resident per CU. The tile width (128 or 160) is the one
   // with the smaller (rounds of resident tiles) x width, since a partial last
@@ -269,15 +270,19 @@ hipError_t launch_t(const TiledArgs &a, hipStream_t stream) {
   // 128 gives 1002 tiles (2 rounds).
   const int64_t slots = 2 * (int64_t)device_cus();
   auto cost = [&](int64_t tn) { return ((a.V + tn - 1) / tn + slots - 1) / slots * tn; };
-  return cost(160) < cost(128) ? launch_tm<128, 160, 2, 2, false, OutT>(a, stream)
-                               : launch_tm<128, 128, 2, 2, false, OutT>(a, stream);
+  return cost(160) < cost(128) ? launch_tm<128, 160, 2, 2, false, F16, OutT>(a, stream)
+                               : launch_tm<128, 128, 2, 2, false, F16, OutT>(a, stream);
 }
 
 }  // namespace
 
-hipError_t launch_tiled(const Bf16Args &a, hipStream_t stream) {
+hipError_t launch_tiled(const GemmArgs &a, hipStream_t stream) {
   const TiledArgs t{a.hidden, a.M, a.H, a.W, nullptr, nullptr, a.V, a.alpha, a.bias, a.out};
-  return a.out_bf16 ? launch_t<uint16_t>(t, stream) : launch_t<float>(t, stream);
+  if (a.in_f16)
+    return a.out_type == OUT_F32 ? launch_t<true, float>(t, stream)
+                                 : launch_t<true, _Float16>(t, stream);
+  return a.out_type == OUT_F32 ? launch_t<false, float>(t, stream)
+                               : launch_t<false, uint16_t>(t, stream);
 }
 
 hipError_t launch_tiled_nvfp4(const Nvfp4Args &a, hipStream_t stream) {
@@ -285,7 +290,7 @@ hipError_t launch_tiled_nvfp4(const Nvfp4Args &a, hipStream_t stream) {
   // 128 x 128 tiles of four waves: measured 12% faster at M = 256 than
   // 256 x 256 or 128 x 256 tiles (more tiles in flight per CU; the decode of
   // each weight tile is repeated once per 128 rows of M).
-  return launch_tm<128, 128, 2, 2, true, uint16_t>(t, stream);
+  return launch_tm<128, 128, 2, 2, true, false, uint16_t>(t, stream);
 }
 
 }  // namespace lmhead

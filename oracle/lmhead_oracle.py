@@ -34,6 +34,11 @@ Readings where the pages are silent (each listed in the design notes):
   (round-to-odd into binary32, then nearest-even into bf16: S. Boldo and
   G. Melquiond, "Emulation of FMA and correctly rounded sums: proved
   algorithms using rounding to odd", IEEE Trans. Computers 57(4), 2008).
+* fp16 inputs (the fast path admits fp16 or bf16 of one dtype -- sglang
+  digest, implementation breakdown): decoded from the IEEE binary16
+  definition; each fp16 x fp16 product is exact in binary64. fp32 output as
+  above; fp16 output: alpha*S (+ b) correctly rounded to binary16, with
+  gradual underflow and overflow to infinity.
 * NVFP4 layout: codes [V, H/2] row-major, element 2i in the low nibble of byte
   i and 2i+1 in the high nibble; one OCP E4M3 scale per 16 consecutive
   elements of a weight row, [V, H/16] row-major; one fp32 per-tensor scale g.
@@ -46,7 +51,10 @@ hand-computed NVFP4 example (tests/golden), exact rational brute force with
 against numpy's int64 matmul, E4M3 decoding checked against torch's
 float8_e4m3fn, bf16 decoding and rounding checked against torch.bfloat16, the
 E2M1 magnitudes of the OCP MX specification, one-hot weights (a gather) and
-zero hidden rows (bias only).
+zero hidden rows (bias only); for fp16, a hand-computed example (tests/golden),
+binary16 decoding against numpy's float16 for every bit pattern, binary16
+rounding against exact rational rounding, rational brute force and integer
+inputs past bf16's range against numpy's int64 matmul.
 """
 from __future__ import annotations
 
@@ -62,6 +70,54 @@ def bf16_to_f64(bits) -> np.ndarray:
     b = np.asarray(bits, dtype=np.uint16)
     with np.errstate(invalid="ignore"):          # NaN patterns widen to NaN
         return (b.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def f16_to_f64(bits) -> np.ndarray:
+    """IEEE binary16: sign bit 15, exponent bits 14..10 (bias 15), fraction
+    bits 9..0. Exponent field 0 is subnormal: value = f * 2^-24; field 31 is
+    infinity (f = 0) or NaN. Widening to binary64 is exact."""
+    b = np.asarray(bits, dtype=np.uint16).astype(np.int64)
+    sign = (b >> 15) & 1
+    e = (b >> 10) & 31
+    f = b & 1023
+    mag = np.where(e == 0, np.ldexp(f.astype(np.float64), -24),
+                   np.ldexp((1024 + f).astype(np.float64), e - 25))
+    mag = np.where(e == 31, np.where(f == 0, np.inf, np.nan), mag)
+    return np.where(sign == 1, -mag, mag).astype(np.float64)
+
+
+def f64_to_f16_correct(x) -> np.ndarray:
+    """binary64 -> binary16 bits, correctly rounded (nearest, ties to even),
+    with gradual underflow and overflow to infinity. Finite inputs only.
+
+    |x| lies in the binade [2^q, 2^(q+1)); binary16 keeps 11 significant bits
+    there, so its spacing is 2^(max(q, -14) - 10) (the subnormals share the
+    spacing of the lowest binade). x / spacing is exact (a power-of-two
+    scaling), rint rounds it to nearest even, and a result of 2^16 or more
+    (beyond the largest finite value 65504 after rounding) is infinity."""
+    x = np.asarray(x, dtype=np.float64)
+    a = np.abs(x)
+    sign = np.where(np.signbit(x), 0x8000, 0).astype(np.int64)
+    _, e = np.frexp(a)                            # a = m 2^e, m in [0.5, 1)
+    q = np.maximum(e - 1, -14)                    # binade of a, floored at the normal minimum
+    n = np.rint(np.ldexp(a, 10 - q)).astype(np.int64)   # significand in units of the spacing
+    # n in [0, 2048]; 2048 carries into the next binade
+    carry = n >= 2048
+    q = np.where(carry, q + 1, q)
+    n = np.where(carry, n >> 1, n)
+    normal = n >= 1024
+    field = np.where(normal, q + 15, 0)
+    bits = np.where(normal, (field << 10) | (n - 1024), n)
+    bits = np.where(field >= 31, 0x7C00, bits)
+    return (sign | bits).astype(np.uint16)
+
+
+def ulp_f16(bits) -> np.ndarray:
+    """Unit in the last place of a binary16 value: 2^(e - 25) for exponent
+    field e, 2^-24 in the subnormal range and at zero."""
+    b = np.asarray(bits, dtype=np.uint16).astype(np.int64)
+    e = (b >> 10) & 31
+    return np.ldexp(1.0, np.maximum(e, 1) - 25)
 
 
 def e2m1_to_f64(code) -> np.ndarray:
@@ -158,13 +214,17 @@ def ulp_bf16(bits) -> np.ndarray:
 # ----------------------------------------------------------------------------
 
 
-def dot_f64(h_bits, w_bits):
+_DECODE = {"bf16": bf16_to_f64, "f16": f16_to_f64}
+
+
+def dot_f64(h_bits, w_bits, in_dtype: str = "bf16"):
     """S[m, v] = sum_k h[m, k] * w[v, k] and A[m, v] = sum_k |h[m, k] * w[v, k]|,
-    both in binary64. Every bf16 x bf16 product is exact in binary64, so the
-    only rounding is that of the binary64 sums (relative 2^-53 per add)."""
-    hf = bf16_to_f64(h_bits)
-    wf = bf16_to_f64(w_bits)
-    return _dot_pair(hf, wf)
+    both in binary64, for bf16 or fp16 ("f16") inputs of one type. Every
+    bf16 x bf16 (8 x 8 significant bits) and fp16 x fp16 (11 x 11) product is
+    exact in binary64, so the only rounding is that of the binary64 sums
+    (relative 2^-53 per add)."""
+    dec = _DECODE[in_dtype]
+    return _dot_pair(dec(h_bits), dec(w_bits))
 
 
 def _dot_pair(hf, wf):
@@ -193,16 +253,29 @@ def logits_bf16(S, alpha: float, bias=None) -> np.ndarray:
     return f64_to_bf16_correct(y)
 
 
-def lmhead_logits(h_bits, w_bits, alpha: float, bias=None, out_dtype: str = "f32"):
-    """Reference logits for bf16 hidden [M, H] and bf16 weight [V, H].
+def logits_f16(S, alpha: float, bias=None) -> np.ndarray:
+    """fp16 logits (bits): alpha*S (+ bias) in binary64, correctly rounded."""
+    y = np.float64(np.float32(alpha)) * np.asarray(S, dtype=np.float64)
+    if bias is not None:
+        y = y + np.asarray(bias, dtype=np.float32).astype(np.float64)
+    return f64_to_f16_correct(y)
 
-    Returns (logits, A): logits are fp32 values for out_dtype "f32" or bf16 bit
-    patterns (uint16) for "bf16"; A = sum_k |h*w| for the tolerance."""
-    S, A = dot_f64(h_bits, w_bits)
+
+def lmhead_logits(h_bits, w_bits, alpha: float, bias=None, out_dtype: str = "f32",
+                  in_dtype: str = "bf16"):
+    """Reference logits for hidden [M, H] and weight [V, H], both bf16 or both
+    fp16 (in_dtype "bf16" / "f16", given as uint16 bit patterns).
+
+    Returns (logits, A): logits are fp32 values for out_dtype "f32", or bf16 /
+    fp16 bit patterns (uint16) for "bf16" / "f16"; A = sum_k |h*w| for the
+    tolerance."""
+    S, A = dot_f64(h_bits, w_bits, in_dtype)
     if out_dtype == "f32":
         return logits_f32(S, alpha, bias), A
     if out_dtype == "bf16":
         return logits_bf16(S, alpha, bias), A
+    if out_dtype == "f16":
+        return logits_f16(S, alpha, bias), A
     raise ValueError(out_dtype)
 
 

@@ -56,8 +56,9 @@ def _load():
         for name in ("synth_normal_bf16", "synth_normal_f32"):
             getattr(lib, name).restype = None
             getattr(lib, name).argtypes = [u64, u64, u64, u64, dbl, dbl, vp, i32]
-        lib.synth_int_bf16.restype = None
-        lib.synth_int_bf16.argtypes = [u64, u64, u64, u64, i32, i32, vp, i32]
+        for name in ("synth_int_bf16", "synth_int_f32"):
+            getattr(lib, name).restype = None
+            getattr(lib, name).argtypes = [u64, u64, u64, u64, i32, i32, vp, i32]
         lib.synth_bytes.restype = None
         lib.synth_bytes.argtypes = [u64, u64, u64, u64, vp, i32]
         lib.synth_uniform_e4m3.restype = None
@@ -105,6 +106,21 @@ def int_bf16(seed, stream, shape, lo, hi, start=0, threads=None) -> np.ndarray:
     _load().synth_int_bf16(seed, stream, start, _n(shape), int(lo), int(hi), out.ctypes.data,
                            threads or default_threads())
     return out
+
+
+def normal_f16(seed, stream, shape, std=1.0, mean=0.0, start=0, threads=None) -> np.ndarray:
+    """fp16 bit patterns (uint16) of mean + std * N(0, 1): the binary32 draw of
+    ``normal_f32`` rounded to binary16 by numpy (nearest even)."""
+    return normal_f32(seed, stream, shape, std, mean, start, threads).astype(np.float16).view(np.uint16)
+
+
+def int_f16(seed, stream, shape, lo, hi, start=0, threads=None) -> np.ndarray:
+    """fp16 bit patterns of integers uniform in [lo, hi] (|lo|, |hi| <= 2048: exact)."""
+    assert -2048 <= lo <= hi <= 2048
+    f = np.empty(shape, dtype=np.float32)
+    _load().synth_int_f32(seed, stream, start, _n(shape), int(lo), int(hi), f.ctypes.data,
+                          threads or default_threads())
+    return f.astype(np.float16).view(np.uint16)
 
 
 def uniform_bytes(seed, stream, shape, start=0, threads=None) -> np.ndarray:

@@ -105,7 +105,7 @@ typedef struct {
   void *out;
 } job_t;
 
-enum { K_NORMAL_BF16 = 0, K_INT_BF16 = 1, K_BYTES = 2, K_UNIFORM_E4M3 = 3, K_NORMAL_F32 = 4 };
+enum { K_NORMAL_BF16 = 0, K_INT_BF16 = 1, K_BYTES = 2, K_UNIFORM_E4M3 = 3, K_NORMAL_F32 = 4, K_INT_F32 = 5 };
 
 static void run_range(const job_t *j, uint64_t lo, uint64_t hi) {
   switch (j->kind) {
@@ -127,6 +127,14 @@ static void run_range(const job_t *j, uint64_t lo, uint64_t hi) {
         uint64_t x = synth_splitmix64_at(j->key, j->start + i);
         double v = j->a + (double)((x >> 32) % span);
         o[i] = f32_to_bf16_bits_rne((float)v);
+      }
+    } break;
+    case K_INT_F32: { /* integers uniform in [a, b] as binary32 (exact for |x| <= 2^24) */
+      float *o = (float *)j->out;
+      uint64_t span = (uint64_t)(j->b - j->a + 1.0);
+      for (uint64_t i = lo; i < hi; ++i) {
+        uint64_t x = synth_splitmix64_at(j->key, j->start + i);
+        o[i] = (float)(j->a + (double)((x >> 32) % span));
       }
     } break;
     case K_BYTES: { /* uniform bytes: every bit independent */
@@ -201,6 +209,13 @@ void synth_normal_f32(uint64_t seed, uint64_t stream, uint64_t start, uint64_t n
 void synth_int_bf16(uint64_t seed, uint64_t stream, uint64_t start, uint64_t n, int lo, int hi,
                     uint16_t *out, int threads) {
   job_t j = {K_INT_BF16, synth_key(seed, stream), start, n, (double)lo, (double)hi, out};
+  run(&j, threads);
+}
+
+/* binary32 integers drawn uniformly from [lo, hi]. */
+void synth_int_f32(uint64_t seed, uint64_t stream, uint64_t start, uint64_t n, int lo, int hi,
+                   float *out, int threads) {
+  job_t j = {K_INT_F32, synth_key(seed, stream), start, n, (double)lo, (double)hi, out};
   run(&j, threads);
 }
 

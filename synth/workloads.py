@@ -14,7 +14,8 @@ from dataclasses import dataclass, field
 import numpy as np
 
 from . import (STREAM_BIAS, STREAM_CODES, STREAM_HIDDEN, STREAM_SCALES, STREAM_WEIGHT,
-               int_bf16, normal_bf16, normal_f32, uniform_bytes, uniform_e4m3)
+               int_bf16, int_f16, normal_bf16, normal_f16, normal_f32, uniform_bytes,
+               uniform_e4m3)
 
 W_STD = 0.02      # weight draws N(0, 0.02): 0.02 read as the standard deviation
 H_STD = 1.0       # hidden draws N(0, 1)
@@ -32,7 +33,8 @@ class Workload:
     alphas: tuple
     seed: int
     bias: bool = False
-    out_dtype: str = "f32"          # "f32" or "bf16"
+    out_dtype: str = "f32"          # "f32", or the input type
+    in_dtype: str = "bf16"          # "bf16" or "f16" (hidden and weight alike)
     nvfp4: bool = False
     g: float = 1.0
     notes: str = field(default="", compare=False)
@@ -55,31 +57,41 @@ NVFP4 = Workload("nvfp4", H=2048, V=151936, Ms=(1, 16, 64, 256), alphas=(1.0,), 
                  out_dtype="bf16", nvfp4=True, g=NVFP4_G,
                  notes="W4A16 NVFP4 head, bf16 out, 64-row blocks")
 
-ALL = {w.name: w for w in (TINY, DECODE, PREFILL, SPEC, NVFP4)}
+F16 = Workload("f16", H=4096, V=128256, Ms=(1, 64, 2048), alphas=(1.0 / 8,), seed=6,
+              in_dtype="f16",
+              notes="fp16 hidden and weight (the fast path's other input type), fp32 out; "
+                    "decode rows and one prefill batch")
+
+ALL = {w.name: w for w in (TINY, DECODE, PREFILL, SPEC, NVFP4, F16)}
+
+
+def _normal(w: Workload):
+    return normal_f16 if w.in_dtype == "f16" else normal_bf16
 
 
 def hidden(w: Workload, M: int | None = None) -> np.ndarray:
-    """bf16 bits [M, H] of N(0, 1)."""
+    """bf16 (or fp16) bits [M, H] of N(0, 1)."""
     M = w.M if M is None else M
-    return normal_bf16(w.seed, STREAM_HIDDEN, (M, w.H), std=H_STD)
+    return _normal(w)(w.seed, STREAM_HIDDEN, (M, w.H), std=H_STD)
 
 
 def hidden_rows(w: Workload, rows) -> np.ndarray:
     rows = np.asarray(rows, dtype=np.int64)
     out = np.empty((len(rows), w.H), dtype=np.uint16)
     for i, r in enumerate(rows):
-        out[i] = normal_bf16(w.seed, STREAM_HIDDEN, (w.H,), std=H_STD, start=int(r) * w.H, threads=1)
+        out[i] = _normal(w)(w.seed, STREAM_HIDDEN, (w.H,), std=H_STD, start=int(r) * w.H,
+                            threads=1)
     return out
 
 
 def weight(w: Workload) -> np.ndarray:
-    """bf16 bits [V, H] of N(0, 0.02)."""
-    return normal_bf16(w.seed, STREAM_WEIGHT, (w.V, w.H), std=W_STD)
+    """bf16 (or fp16) bits [V, H] of N(0, 0.02)."""
+    return _normal(w)(w.seed, STREAM_WEIGHT, (w.V, w.H), std=W_STD)
 
 
 def weight_rows(w: Workload, v0: int, nv: int) -> np.ndarray:
-    """bf16 bits of weight rows [v0, v0 + nv) only."""
-    return normal_bf16(w.seed, STREAM_WEIGHT, (nv, w.H), std=W_STD, start=v0 * w.H)
+    """bf16 (or fp16) bits of weight rows [v0, v0 + nv) only."""
+    return _normal(w)(w.seed, STREAM_WEIGHT, (nv, w.H), std=W_STD, start=v0 * w.H)
 
 
 def bias(w: Workload) -> np.ndarray | None:
@@ -108,3 +120,12 @@ def int_hidden(seed: int, M: int, H: int, lo: int = -4, hi: int = 4) -> np.ndarr
 
 def int_weight(seed: int, V: int, H: int, lo: int = -4, hi: int = 4) -> np.ndarray:
     return int_bf16(seed, STREAM_WEIGHT, (V, H), lo, hi)
+
+
+def int_hidden_f16(seed: int, M: int, H: int, lo: int = -1000, hi: int = 1000) -> np.ndarray:
+    """Integer-valued fp16 hidden; magnitudes past 256 are not bf16 values."""
+    return int_f16(seed, STREAM_HIDDEN, (M, H), lo, hi)
+
+
+def int_weight_f16(seed: int, V: int, H: int, lo: int = -4, hi: int = 4) -> np.ndarray:
+    return int_f16(seed, STREAM_WEIGHT, (V, H), lo, hi)

@@ -115,3 +115,24 @@ def check_bf16(gpu_bits, ref_bits, A, scale, ulp_fn, rel=2e-5, what=""):
                              + ", ".join(f"{tuple(i)}: gpu={g[tuple(i)]!r} ref={r[tuple(i)]!r}"
                                          for i in idx))
     return int(np.sum(err > ulp))
+
+
+def check_f16(gpu_bits, ref_bits, A, scale, ulp_fn, rel=2e-5, what=""):
+    """fp16 parity, the bound of ``check_bf16`` with fp16 ulps: |gpu - ref| <=
+    max(1 ulp(ref), rel*|scale|*A); an infinite reference (overflow) must be
+    met by the same infinity. Returns the count outside the strict 1-ulp bound."""
+    g = np.asarray(gpu_bits, dtype=np.uint16).view(np.float16).astype(np.float64)
+    r = np.asarray(ref_bits, dtype=np.uint16).view(np.float16).astype(np.float64)
+    inf = np.isinf(r)
+    if not np.array_equal(g[inf], r[inf]):
+        raise AssertionError(f"{what}: overflow to infinity not matched")
+    g, r = g[~inf], r[~inf]
+    ulp = np.asarray(ulp_fn(ref_bits))[~inf]
+    err = np.abs(g - r)
+    bound = np.maximum(ulp, rel * abs(scale) * np.asarray(A, dtype=np.float64)[~inf])
+    bad = ~(err <= bound)
+    if bad.any():
+        idx = np.flatnonzero(bad)[:5]
+        raise AssertionError(f"{what}: {int(bad.sum())} fp16 elements out of tolerance, e.g. "
+                             + ", ".join(f"gpu={g[i]!r} ref={r[i]!r}" for i in idx))
+    return int(np.sum(err > ulp))

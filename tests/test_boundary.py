@@ -74,6 +74,27 @@ def call4(hidden=FAKE, M=4, H=64, codes=FAKE, scales=FAKE, g=1.0, V=100, alpha=1
                                            None)
 
 
+def callx(hidden=FAKE, M=4, H=64, W=FAKE, V=100, alpha=1.0, bias=None, din=1, dout=0, out=FAKE,
+          path=-2):
+    return _lib.load().lmhead_logits_ex(hidden, M, H, W, V, alpha, bias, din, dout, out, None, path)
+
+
+def test_dtype_pairs_of_the_general_entry_point():
+    F32, BF16, F16 = _lib.LMHEAD_F32, _lib.LMHEAD_BF16, _lib.LMHEAD_F16
+    NH, E = _lib.NOT_HANDLED, _lib.ERR_INVALID
+    # supported pairs pass every host check (M = 0: nothing is launched)
+    for din, dout in ((BF16, F32), (BF16, BF16), (F16, F32), (F16, F16)):
+        assert callx(hidden=None, W=None, out=None, M=0, din=din, dout=dout) == _lib.OK
+        assert callx(hidden=None, din=din, dout=dout) == E
+    # fp32 inputs and mixed 16-bit types are the caller's fallback
+    for din, dout in ((F32, F32), (BF16, F16), (F16, BF16)):
+        assert callx(din=din, dout=dout) == NH
+    assert callx(din=3) == E and callx(dout=-1) == E
+    assert callx(path=_lib.PATH_NVFP4) == E
+    # the bf16 entry points refuse fp16 logits
+    assert call(dt=F16) == E
+
+
 def test_m_zero_is_ok_and_launches_nothing():
     assert call(hidden=None, W=None, out=None, M=0) == _lib.OK
     assert call4(hidden=None, codes=None, scales=None, out=None, M=0) == _lib.OK

@@ -11,7 +11,7 @@ import torch
 import lm_head_logits_amd as L
 import oracle
 import synth.workloads as wl
-from gpu_util import DEV, bf16_dev, f32_dev, host_bits, host_f32, say, u8_dev
+from gpu_util import DEV, bf16_dev, f16_dev, f32_dev, host_bits, host_f32, say, u8_dev
 from helpers import check_bf16, check_f32
 
 pytestmark = pytest.mark.gpu
@@ -160,4 +160,33 @@ def test_nvfp4_rows_invariant(nvfp4):
     full = L.logits_nvfp4(hd, cd, sd, w.g, 1.0)
     for M in (1, 2, 15, 16, 17, 63, 64, 65, 128, 255):
         part = L.logits_nvfp4(hd[:M].contiguous(), cd, sd, w.g, 1.0)
+        assert torch.equal(ibits(part), ibits(full[:M])), M
+
+
+@pytest.fixture(scope="module")
+def f16():
+    w = wl.F16
+    say("generate fp16 inputs H=4096 V=128256")
+    h, W = wl.hidden(w), wl.weight(w)
+    return w, h, W, f16_dev(h), f16_dev(W)
+
+
+@pytest.mark.parametrize("M", wl.F16.Ms)
+def test_f16_parity(f16, M):
+    w, h, W, hd, Wd = f16
+    say(f"fp16 M={M}")
+    alpha = w.alphas[0]
+    out = L.logits(hd[:M], Wd, alpha)
+    rows, cols = row_sample(M), col_sample(w.V, n=1024, seed=M)
+    got = host_f32(out[torch.as_tensor(rows, device=DEV)])
+    ref, A = oracle.lmhead_logits(h[rows], W[cols], alpha, None, "f32", in_dtype="f16")
+    ratio, exact = check_f32(got[:, cols], ref, A, what=f"fp16 M={M}")
+    say(f"  max err/bound {ratio:.3f}, bit-exact fraction {exact:.3f}")
+
+
+def test_f16_rows_invariant(f16):
+    w, h, W, hd, Wd = f16
+    full = L.logits(hd, Wd, w.alphas[0])
+    for M in (1, 7, 64, 65, 300):
+        part = L.logits(hd[:M].contiguous(), Wd, w.alphas[0])
         assert torch.equal(ibits(part), ibits(full[:M])), M

@@ -12,7 +12,8 @@ import pytest
 import torch
 
 import oracle
-from helpers import (f32_bits_to_bf16_bits_exact, load_golden, num, rne32, rne_bf16)
+from helpers import (f32_bits_to_bf16_bits_exact, load_golden, num, rne32, rne_bf16,
+                     round_fraction)
 
 
 def _rows(g, key):
@@ -269,3 +270,129 @@ def test_ulp_bf16():
     assert oracle.ulp_bf16(np.uint16(0x4000)) == 2.0 ** -6       # 2.0
     assert oracle.ulp_bf16(np.uint16(0xBF80)) == 2.0 ** -7       # -1.0
     assert oracle.ulp_bf16(np.uint16(0x0000)) == 2.0 ** -133
+
+
+# ---------------------------------------------------------------------------
+# fp16 inputs and outputs.
+# ---------------------------------------------------------------------------
+
+def _bits(g, key):
+    return np.array([[int(x, 16) for x in row] for row in g[key]], dtype=np.uint16)
+
+
+def rne_f16(q: Fraction) -> Fraction:
+    return round_fraction(q, 11, -14)
+
+
+def _f16_bits_of(q: Fraction, negative: bool) -> int:
+    """binary16 bits of the rounded value q of an exact result with the given
+    sign: +-inf past the largest finite value (nearest-even overflow), a
+    signed zero when the result rounded to zero."""
+    sign = 0x8000 if negative else 0
+    if abs(q) >= 65520:          # 65504 + half its spacing: rounds past the largest finite
+        return 0x7C00 | sign
+    return int(np.float16(float(abs(q))).view(np.uint16)) | sign
+
+
+def test_hand_example_f16():
+    g = load_golden("hand_f16.txt")
+    h, w = _bits(g, "hidden"), _bits(g, "weight")
+    alpha = num(g["alpha"][0][0])
+    b = _rows(g, "bias")[0].astype(np.float32)
+    S, _ = oracle.dot_f64(h, w, "f16")
+    assert np.array_equal(S, _rows(g, "dot"))
+    for bias, key in ((None, "nobias"), (b, "withbias")):
+        got32, _ = oracle.lmhead_logits(h, w, alpha, bias, "f32", in_dtype="f16")
+        want32 = _rows(g, key + "_f32").astype(np.float32)
+        assert np.array_equal(got32.view(np.uint32), want32.view(np.uint32)), key
+        got16, _ = oracle.lmhead_logits(h, w, alpha, bias, "f16", in_dtype="f16")
+        assert np.array_equal(got16, _bits(g, key + "_f16")), key
+    # read as bf16 the same bits give other products: the input type matters
+    S_bf, _ = oracle.dot_f64(h, w, "bf16")
+    assert not np.array_equal(S_bf, S)
+
+
+def test_f16_decode_exhaustive_vs_numpy():
+    bits = np.arange(65536, dtype=np.uint16)
+    ours = oracle.f16_to_f64(bits)
+    theirs = bits.view(np.float16).astype(np.float64)
+    assert np.array_equal(ours, theirs, equal_nan=True)
+    assert np.array_equal(np.signbit(ours), np.signbit(theirs))
+    # landmarks of the format: 1, smallest subnormal, smallest normal, largest finite
+    assert oracle.f16_to_f64(np.uint16(0x3C00)) == 1.0
+    assert oracle.f16_to_f64(np.uint16(0x0001)) == 2.0 ** -24
+    assert oracle.f16_to_f64(np.uint16(0x0400)) == 2.0 ** -14
+    assert oracle.f16_to_f64(np.uint16(0x7BFF)) == 65504.0
+    assert oracle.f16_to_f64(np.uint16(0xFC00)) == -np.inf
+
+
+def test_f64_to_f16_correct_rounding_vs_fractions():
+    rng = np.random.default_rng(13)
+    xs = list(rng.normal(0, 1, 2000) * np.exp2(rng.integers(-28, 17, 2000)))
+    # exact ties and their neighbours in normal and subnormal binades
+    for _ in range(300):
+        e = int(rng.integers(-24, 16))
+        n = int(rng.integers(1024, 2048))
+        tie = (Fraction(n) + Fraction(1, 2)) * Fraction(2) ** (max(e, -14) - 10)
+        for d in (Fraction(1, 2**30), -Fraction(1, 2**30), 0):
+            xs.append(float(tie + d * Fraction(2) ** e))
+    # overflow threshold: 65504 + 16 is the tie between 65504 and 2^16
+    xs += [65504.0, 65519.99, 65520.0, 65536.0, 1e6, -65520.0, -65519.0, 0.0, -0.0,
+           2.0 ** -25, 2.0 ** -25 * 1.0000001, 2.0 ** -26, 3 * 2.0 ** -25]
+    xs = np.array(xs, dtype=np.float64)
+    got = oracle.f64_to_f16_correct(xs)
+    want = np.array([_f16_bits_of(rne_f16(Fraction(float(x))), bool(np.signbit(x))) for x in xs],
+                    dtype=np.uint16)
+    assert np.array_equal(got, want)
+
+
+def test_ulp_f16():
+    assert oracle.ulp_f16(np.uint16(0x3C00)) == 2.0 ** -10     # 1.0
+    assert oracle.ulp_f16(np.uint16(0x4000)) == 2.0 ** -9      # 2.0
+    assert oracle.ulp_f16(np.uint16(0xBC00)) == 2.0 ** -10     # -1.0
+    assert oracle.ulp_f16(np.uint16(0x7BFF)) == 32.0           # 65504
+    assert oracle.ulp_f16(np.uint16(0x0001)) == 2.0 ** -24     # subnormal
+
+
+@pytest.mark.parametrize("seed", range(20))
+def test_bruteforce_f16_vs_fractions(seed):
+    rng = np.random.default_rng(1000 + seed)
+    M, V = (int(x) for x in rng.integers(1, 4, 2))
+    H = int(rng.integers(1, 9))
+    h = rng.normal(0, 1, (M, H)).astype(np.float16).view(np.uint16)
+    w = (rng.normal(0, 1, (V, H)) * np.exp2(rng.integers(-12, 3, (V, H)))).astype(
+        np.float16).view(np.uint16)
+    alpha = float(np.float32(rng.choice([1.0, 0.25, 1 / 3, 0.7, 1 / 16])))
+    bias = rng.normal(0, 0.1, V).astype(np.float32) if seed % 2 else None
+    hq = [[Fraction(float(x)) for x in row] for row in h.view(np.float16)]
+    wq = [[Fraction(float(x)) for x in row] for row in w.view(np.float16)]
+    got32, A = oracle.lmhead_logits(h, w, alpha, bias, "f32", in_dtype="f16")
+    got16, _ = oracle.lmhead_logits(h, w, alpha, bias, "f16", in_dtype="f16")
+    for m in range(M):
+        for v in range(V):
+            S = sum(a * b for a, b in zip(hq[m], wq[v]))
+            Aq = sum(abs(a * b) for a, b in zip(hq[m], wq[v]))
+            assert abs(A[m, v] - float(Aq)) <= 1e-15 * float(Aq)
+            r = rne32(S)
+            r = rne32(r * Fraction(alpha))
+            if bias is not None:
+                r = rne32(r + Fraction(float(bias[v])))
+            assert got32[m, v] == np.float32(float(r)), (m, v)
+            y = Fraction(alpha) * S + (Fraction(float(bias[v])) if bias is not None else 0)
+            # an exact zero sum is +0 in round-to-nearest
+            assert got16[m, v] == _f16_bits_of(rne_f16(y), y < 0), (m, v)
+
+
+def test_integer_f16_inputs_match_int64_matmul():
+    import synth.workloads as wl
+    M, V, H = 4, 29, 2048
+    h = wl.int_hidden_f16(9, M, H)           # magnitudes up to 1000: not bf16 values
+    w = wl.int_weight_f16(9, V, H)
+    hi = h.view(np.float16).astype(np.int64)
+    wi = w.view(np.float16).astype(np.int64)
+    assert np.abs(hi).max() > 256
+    exact = hi @ wi.T
+    for alpha in (1.0, 0.125):
+        got, _ = oracle.lmhead_logits(h, w, alpha, None, "f32", in_dtype="f16")
+        want = (exact.astype(np.float32) * np.float32(alpha)).astype(np.float32)
+        assert np.array_equal(got, want)

@@ -94,3 +94,15 @@ def test_nvfp4_byte_model():
     bf16_bytes = V * H * 2
     nvfp4_bytes = V * H // 2 + V * H // 16
     assert abs(bf16_bytes / nvfp4_bytes - 3.5) < 0.1
+
+
+def test_f16_generators():
+    x = synth.normal_f16(3, 1, (1_000_000,), std=0.02).view(np.float16).astype(np.float64)
+    assert abs(x.mean()) < 1e-4 and abs(x.std() - 0.02) < 2e-4
+    # the fp16 draw is the fp32 draw rounded to nearest even
+    f = synth.normal_f32(3, 1, (1000,), std=0.02)
+    assert np.array_equal(synth.normal_f16(3, 1, (1000,), std=0.02), f.astype(np.float16).view(np.uint16))
+    i = synth.int_f16(4, 1, (200000,), -1000, 1000).view(np.float16).astype(np.float64)
+    assert i.min() == -1000 and i.max() == 1000 and np.all(i == np.round(i))
+    assert np.array_equal(synth.int_f16(4, 1, (100,), -1000, 1000, start=500, threads=1),
+                          synth.int_f16(4, 1, (600,), -1000, 1000, threads=3)[500:])
