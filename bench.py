@@ -7,8 +7,8 @@ one lmhead_logits call for each M in {1, 2, 8, 32, 64}. The headline value is
 the whole step's algorithmic HBM throughput (weight read once + hidden +
 output written, divided by the step time). The other workloads -- prefill
 (M=2048), spec-decode (M=128 with bias), the NVFP4 head (M in 1, 16, 64,
-256) and fp16 inputs (M in 1, 64, 2048) -- are timed after it and reported
-alongside.
+256), fp16 inputs (M in 1, 64, 2048) and the row-reduction epilogue (decode
+M = 64, spec M = 128) -- are timed after it and reported alongside.
 
 Inputs are generated on the host from the seeded generator, copied to HBM
 before timing, and never touched by the timed region. Timing uses HIP events
@@ -236,6 +236,32 @@ def bench_f16(torch, L, wl, dev, warmup, steps):
     return res
 
 
+def bench_rowreduce(torch, L, wl, dev, warmup, steps):
+    """The row-reduction epilogue (max, argmax, sum of exp) with no logits
+    written, against the plain call that writes fp32 logits: decode M = 64
+    and the spec-decode target M = 128 (with bias)."""
+    res = {}
+    for w, M, alpha, tag in ((wl.DECODE, 64, wl.DECODE.alphas[1], "decode_M64"),
+                             (wl.SPEC, 128, wl.SPEC.alphas[0], "spec_M128")):
+        log(f"rowreduce: {tag}")
+        h, W, b = wl.hidden(w, M), wl.weight(w), wl.bias(w)
+        hd, Wd = to_dev_bf16(torch, h, dev), to_dev_bf16(torch, W, dev)
+        bd = torch.from_numpy(b).to(dev) if b is not None else None
+        out = torch.empty((M, w.V), dtype=torch.float32, device=dev)
+        ws = torch.empty(L.rowreduce_workspace_bytes(M, w.V), dtype=torch.uint8, device=dev)
+        fns = [lambda: L.logits(hd, Wd, alpha, bd, out=out),
+               lambda: L.logits_rowreduce(hd, Wd, alpha, bd, workspace=ws)]
+        _, _, per = timed_calls(torch, fns, warmup, steps)
+        plain_us, red_us = (1e3 * float(np.mean(p)) for p in per)
+        by_red = bytes_bf16(M, w.H, w.V, 0, b is not None) + 2 * ws.numel() + 12 * M
+        res[tag] = {"plain_us": round(plain_us, 2), "rowreduce_us": round(red_us, 2),
+                    "rowreduce_GBps": round(by_red / red_us / 1e3, 1),
+                    "rowreduce_frac_hbm": round(by_red / red_us / 1e3 / HBM_PEAK_GBPS, 4)}
+        del hd, Wd, out, ws
+        torch.cuda.empty_cache()
+    return res
+
+
 def bench_copy(torch, dev, warmup, steps, nbytes=1 << 30):
     """A plain device-to-device copy of `nbytes` (torch's copy kernel): reads
     and writes exactly nbytes, so the HBM counters read on it give the scale
@@ -290,7 +316,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--only", choices=["decode", "prefill", "spec", "nvfp4", "f16", "copy", "all"],
+    ap.add_argument("--only", choices=["decode", "prefill", "spec", "nvfp4", "f16", "rowreduce",
+                                       "copy", "all"],
                     default="all",
                     help="run one workload only (for profiling; 'copy' is the HBM counter "
                          "calibration); the headline line needs decode")
@@ -315,6 +342,7 @@ def main():
               "spec": lambda: bench_spec(torch, L, wl, dev, args.warmup, args.steps),
               "nvfp4": lambda: bench_nvfp4(torch, L, wl, dev, args.warmup, args.steps),
               "f16": lambda: bench_f16(torch, L, wl, dev, args.warmup, args.steps),
+              "rowreduce": lambda: bench_rowreduce(torch, L, wl, dev, args.warmup, args.steps),
               "copy": lambda: bench_copy(torch, dev, args.warmup, args.steps)}[args.only]
         print(json.dumps({"workload": args.only, "result": fn()}), flush=True)
         return
@@ -330,6 +358,9 @@ def main():
         torch.cuda.empty_cache()
     if run("f16"):
         extra["f16_inputs"] = bench_f16(torch, L, wl, dev, args.warmup, args.steps)
+        torch.cuda.empty_cache()
+    if run("rowreduce"):
+        extra["rowreduce"] = bench_rowreduce(torch, L, wl, dev, args.warmup, args.steps)
 
     w = dec["w"]
     step_ms = dec["step_ms"]

@@ -46,6 +46,7 @@
 #ifndef LMHEAD_H
 #define LMHEAD_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -126,6 +127,48 @@ lmhead_status lmhead_logits_path(const void *hidden, int64_t M, int64_t H, const
 lmhead_status lmhead_logits_ex(const void *hidden, int64_t M, int64_t H, const void *W, int64_t V,
                                float alpha, const float *bias, lmhead_dtype in_dtype,
                                lmhead_dtype out_dtype, void *out, void *stream, int path);
+
+/* The projection with a row-reduction epilogue: for every row m, over the
+ * fp32 logits t[m, v] the call computes (the epilogue values of
+ * lmhead_logits_ex, before any rounding to a 16-bit out_dtype):
+ *   row_max[m]    = max over v of t[m, v]
+ *   row_argmax[m] = the lowest v with t[m, v] == row_max[m]
+ *   row_sumexp[m] = sum over v of exp(t[m, v] - row_max[m])   (>= 1)
+ * so that the row's log-sum-exp is row_max + log(row_sumexp) and
+ * softmax(t)[m, v] = exp(t[m, v] - row_max[m]) / row_sumexp[m]. These feed
+ * the target and draft heads' acceptance distributions (vLLM PR 49120,
+ * section Purpose) and greedy selection whose ties keep the lowest index, as
+ * a stable descending sort does (tokenspeed PR 720, summary and review
+ * thread). They are computed inside the GEMM's epilogue, so the [M, V] logits
+ * need not be written at all.
+ *   hidden, W, alpha, bias, in_dtype, out_dtype, path   as in lmhead_logits_ex
+ *   out         [M, V] of out_dtype, or NULL: the logits are then not written
+ *   row_max     fp32 [M]                          (device, written)
+ *   row_argmax  int32 [M]                         (device, written)
+ *   row_sumexp  fp32 [M]                          (device, written)
+ *   workspace   device memory of at least lmhead_rowreduce_workspace_bytes(M, V)
+ *               bytes, 16-byte aligned; the call overwrites it (it holds one
+ *               16-byte partial per row and 16-column block) and it must not be
+ *               in use by other work until this call's work has finished
+ * row_max and row_argmax are exact: the maximum and the lowest argmax of the
+ * fp32 logits lmhead_logits_ex writes (a zero maximum present with both signs
+ * may be returned as either zero). row_sumexp is accumulated at fp32 in a
+ * fixed order that depends only on V, each exponential taken as
+ * 2^(x log2 e). All three are the same, bit for bit, whatever the row count
+ * of the call and the path.
+ * Returns as lmhead_logits_ex; LMHEAD_ERR_INVALID also for a NULL row output
+ * or workspace, or a workspace smaller than required (M > 0); LMHEAD_ERR_ALIGN
+ * for a misaligned workspace or row output (4-byte). */
+lmhead_status lmhead_logits_rowreduce(const void *hidden, int64_t M, int64_t H, const void *W,
+                                      int64_t V, float alpha, const float *bias,
+                                      lmhead_dtype in_dtype, lmhead_dtype out_dtype, void *out,
+                                      float *row_max, int32_t *row_argmax, float *row_sumexp,
+                                      void *workspace, size_t workspace_bytes, void *stream,
+                                      int path);
+
+/* Host-only: bytes of workspace lmhead_logits_rowreduce needs for (M, V):
+ * 16 * M * ceil(V / 16); 0 when M or V is outside the shape contract. */
+size_t lmhead_rowreduce_workspace_bytes(int64_t M, int64_t V);
 
 /* The NVFP4 W4A16 head (bf16 logits).
  *   hidden       bf16 [M, H]                    (device, read)

@@ -16,7 +16,7 @@ from . import _lib
 from ._lib import (LMHEAD_BF16, LMHEAD_F16, LMHEAD_F32, NOT_HANDLED, OK, PATH_AUTO, PATH_NONE,
                    PATH_NVFP4, PATH_SKINNY, PATH_TILED)
 
-__all__ = ["logits", "logits_nvfp4", "shape_ok", "path_for", "status_string", "version",
+__all__ = ["logits", "logits_rowreduce", "rowreduce_workspace_bytes", "logits_nvfp4", "shape_ok", "path_for", "status_string", "version",
            "LmHeadError", "NotHandled", "PATH_SKINNY", "PATH_TILED", "PATH_NVFP4", "PATH_AUTO",
            "PATH_NONE"]
 
@@ -108,6 +108,58 @@ def logits(hidden: torch.Tensor, weight: torch.Tensor, alpha: float = 1.0, bias=
             out.data_ptr(), _stream_handle(hidden.device, stream), _PATHS[path])
     _check(st, "lmhead_logits_ex")
     return out
+
+
+def rowreduce_workspace_bytes(M: int, V: int) -> int:
+    return int(_lib.load().lmhead_rowreduce_workspace_bytes(M, V))
+
+
+def logits_rowreduce(hidden: torch.Tensor, weight: torch.Tensor, alpha: float = 1.0, bias=None,
+                     out_dtype=torch.float32, out: torch.Tensor | None = None, *,
+                     write_logits: bool = False, workspace: torch.Tensor | None = None,
+                     path: str = "auto", stream=None):
+    """Row reduction of alpha * hidden @ weight.T (+ bias) inside the GEMM's
+    epilogue (lmhead_logits_rowreduce): returns (row_max fp32 [M], row_argmax
+    int32 [M], row_sumexp fp32 [M], logits or None). The logits [M, V] are
+    written only when `out` is given or `write_logits` is true. `workspace`
+    (a byte tensor of at least rowreduce_workspace_bytes(M, V)) is allocated
+    here when not given."""
+    _need(hidden.is_cuda and weight.is_cuda, "hidden and weight must be device tensors")
+    _need(hidden.dtype in _DTYPES and weight.dtype in _DTYPES and out_dtype in _DTYPES,
+          "dtypes must be float32, bfloat16 or float16")
+    _need(hidden.dim() == 2 and weight.dim() == 2, "hidden [M, H] and weight [V, H] are 2-D")
+    _need(hidden.is_contiguous() and weight.is_contiguous(), "inputs must be contiguous")
+    M, H = hidden.shape
+    V, H2 = weight.shape
+    _need(H == H2, f"hidden has H={H}, weight has H={H2}")
+    in_code = _DTYPES[hidden.dtype] if hidden.dtype == weight.dtype else LMHEAD_F32
+    dev = hidden.device
+    if bias is not None:
+        _need(bias.is_cuda and bias.dtype == torch.float32 and bias.shape == (V,)
+              and bias.is_contiguous(), "bias must be a contiguous fp32 device tensor [V]")
+    if out is None and write_logits:
+        out = torch.empty((M, V), dtype=out_dtype, device=dev)
+    if out is not None:
+        _need(out.is_cuda and out.dtype == out_dtype and out.shape == (M, V) and out.is_contiguous(),
+              "out must be a contiguous [M, V] device tensor of out_dtype")
+    need = rowreduce_workspace_bytes(M, V)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+    _need(workspace.is_cuda and workspace.is_contiguous(), "workspace must be a contiguous device tensor")
+    row_max = torch.empty(M, dtype=torch.float32, device=dev)
+    row_argmax = torch.empty(M, dtype=torch.int32, device=dev)
+    row_sumexp = torch.empty(M, dtype=torch.float32, device=dev)
+    _same_device(hidden, weight, bias, out, workspace)
+    with torch.cuda.device(dev):
+        st = _lib.load().lmhead_logits_rowreduce(
+            hidden.data_ptr(), M, H, weight.data_ptr(), V, float(alpha),
+            bias.data_ptr() if bias is not None else None, in_code, _DTYPES[out_dtype],
+            out.data_ptr() if out is not None else None, row_max.data_ptr(),
+            row_argmax.data_ptr(), row_sumexp.data_ptr(), workspace.data_ptr(),
+            workspace.numel() * workspace.element_size(), _stream_handle(dev, stream),
+            _PATHS[path])
+    _check(st, "lmhead_logits_rowreduce")
+    return row_max, row_argmax, row_sumexp, out
 
 
 def logits_nvfp4(hidden: torch.Tensor, codes: torch.Tensor, scales: torch.Tensor,

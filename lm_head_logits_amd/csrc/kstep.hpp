@@ -210,4 +210,116 @@ __device__ __forceinline__ void store_blocks(Acc &&acc, OutT *out, int64_t rbase
   }
 }
 
+// ---------------------------------------------------------------------------
+// Row-reduction epilogue: instead of (or besides) the logits, per-row
+// partials over each 16-column block -- the block's largest logit t_max, the
+// lowest column holding it, and the sum of exp(t - t_max) over the block's
+// columns -- for the softmax quantities of a row (its maximum, argmax with
+// the lowest index winning ties, and log-sum-exp) without a second pass over
+// [M, V] logits. The logit t is the epilogue value above, so the partials
+// reduce exactly the fp32 logits the plain call writes.
+//
+// A block's partial depends only on the block's 16 logits and their lane
+// positions (column c0 + li in lane 16 g + li): the maximum and its column
+// are exact, and the sum is a fixed butterfly over the 16 lanes, in which
+// both partners of every step add the same two values (the same bits). So the
+// partials, and the combined row results, are the same whichever kernel ran
+// and however many rows the call had. (When the maximum is a zero present
+// with both signs, the sign of the zero stored is the hardware maximum's.)
+//
+// Record of row m, block cb at part[m * ncb + cb] (ncb = ceil(V / 16)).
+// ---------------------------------------------------------------------------
+// Written and read as a struct: with this compiler, __builtin_bit_cast of a
+// vector element (v.y of a u32x4) compiled to a read of element 0.
+struct alignas(16) RowPart {
+  float m;    // the block's largest logit
+  float s;    // sum over the block's columns of exp(logit - m)
+  int32_t i;  // lowest column holding m
+  int32_t pad;
+};
+
+// (value, column) maximum with the lowest column winning ties; the same
+// answer for either argument order.
+__device__ __forceinline__ void max_lowest(float &m, int &mi, float om, int oi) {
+  if (om > m || (om == m && oi < mi)) {
+    m = om;
+    mi = oi;
+  }
+}
+
+// Butterfly over the 16 lanes of a DPP row (lanes 16 g .. 16 g + 15) by data
+// movement within the row: partner lane l ^ 1, l ^ 2 (quad permutations),
+// then the mirror inside 8 lanes and inside 16 lanes. The four steps pair the
+// same lanes' values as an xor butterfly 1, 2, 4, 8 does (pairs, quads,
+// halves, rows), and each step combines two values with an operation for
+// which both partners compute the same bits, so every lane ends with the
+// same result.
+constexpr int DPP_QUAD_SWAP1 = 0xB1;        // quad_perm [1, 0, 3, 2]
+constexpr int DPP_QUAD_SWAP2 = 0x4E;        // quad_perm [2, 3, 0, 1]
+constexpr int DPP_ROW_HALF_MIRROR = 0x141;  // lane i <-> 7 - i within 8
+constexpr int DPP_ROW_MIRROR = 0x140;       // lane i <-> 15 - i within 16
+
+template <int CTRL>
+__device__ __forceinline__ int dpp(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, false);
+}
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return __builtin_bit_cast(float, dpp<CTRL>(__builtin_bit_cast(int, v)));
+}
+
+// Largest value over the row's 16 lanes. Equal values of opposite zero sign
+// may come back as either zero; nothing below depends on which.
+__device__ __forceinline__ float row16_max(float v) {
+  v = fmaxf(v, dpp<DPP_QUAD_SWAP1>(v));
+  v = fmaxf(v, dpp<DPP_QUAD_SWAP2>(v));
+  v = fmaxf(v, dpp<DPP_ROW_HALF_MIRROR>(v));
+  return fmaxf(v, dpp<DPP_ROW_MIRROR>(v));
+}
+__device__ __forceinline__ int row16_min(int v) {
+  v = min(v, dpp<DPP_QUAD_SWAP1>(v));
+  v = min(v, dpp<DPP_QUAD_SWAP2>(v));
+  v = min(v, dpp<DPP_ROW_HALF_MIRROR>(v));
+  return min(v, dpp<DPP_ROW_MIRROR>(v));
+}
+__device__ __forceinline__ float row16_sum(float v) {
+  v = __fadd_rn(v, dpp<DPP_QUAD_SWAP1>(v));
+  v = __fadd_rn(v, dpp<DPP_QUAD_SWAP2>(v));
+  v = __fadd_rn(v, dpp<DPP_ROW_HALF_MIRROR>(v));
+  return __fadd_rn(v, dpp<DPP_ROW_MIRROR>(v));
+}
+
+// e^x as 2^(x log2 e) (the hardware exp2 of a rounded product).
+__device__ __forceinline__ float exp_fast(float x) { return __expf(x); }
+
+template <int FM, int FN, typename Acc>
+__device__ __forceinline__ void reduce_blocks(Acc &&acc, RowPart *__restrict__ part, int64_t rbase,
+                                              int64_t rows, int64_t cbase, int64_t cend,
+                                              int64_t V, float alpha,
+                                              const float *__restrict__ bias) {
+  const int lane = threadIdx.x & 63;
+  const int li = lane & 15, lg = lane >> 4;
+  const int64_t ncb = (V + 15) / 16;
+  const bool has_bias = bias != nullptr;
+#pragma unroll
+  for (int j = 0; j < FN; ++j) {
+    if (cbase + 16 * j >= cend) break;  // wave-uniform: this and later blocks have no column
+    const int64_t col = cbase + 16 * j + li;
+    const bool ok = col < cend;
+    const float b = (has_bias && ok) ? bias[col] : 0.0f;
+    const int64_t cb = (cbase >> 4) + j;
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float t = ok ? epilogue_v(acc(i, j)[q], alpha, has_bias, b) : -__builtin_inff();
+        const float m = row16_max(t);
+        const int mi = row16_min(ok && t == m ? (int)col : 0x7FFFFFFF);
+        const float e = row16_sum(ok ? exp_fast(__fsub_rn(t, m)) : 0.0f);
+        const int r = 16 * i + 4 * lg + q;  // row within the wave's rows
+        if (li == q && r < rows) part[(rbase + r) * ncb + cb] = RowPart{m, e, mi, 0};
+      }
+  }
+}
+
 }  // namespace lmhead

@@ -19,7 +19,8 @@ struct GemmArgs {
   const float *bias;       // [V] or nullptr
   int in_f16;              // 0: bf16 inputs, 1: fp16 inputs
   OutType out_type;        // OUT_F32, or the input type
-  void *out;               // [M, V]
+  void *out;               // [M, V], or nullptr (no logits written)
+  void *part;              // row-reduction partials, 16 B x [M, ceil(V / 16)], or nullptr
 };
 
 struct Nvfp4Args {
@@ -63,6 +64,10 @@ struct VSplit {
   int nb;
 };
 VSplit vsplit(int64_t ncb, int waves, int nb_max);
+
+// Folds the partials of each row into its (max, argmax, sum of exp(x - max)).
+hipError_t launch_row_combine(const void *part, int64_t M, int64_t V, float *row_max,
+                              int32_t *row_argmax, float *row_sumexp, hipStream_t stream);
 
 hipError_t launch_skinny(const GemmArgs &a, hipStream_t stream);
 hipError_t launch_tiled(const GemmArgs &a, hipStream_t stream);

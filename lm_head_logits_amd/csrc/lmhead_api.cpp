@@ -32,6 +32,45 @@ int auto_path(int64_t M) { return M <= 64 ? LMHEAD_PATH_SKINNY : LMHEAD_PATH_TIL
 
 bool known_dtype(int d) { return d == LMHEAD_F32 || d == LMHEAD_BF16 || d == LMHEAD_F16; }
 
+// Host checks shared by the 16-bit entry points, in the order: shape, dtype
+// and path values, dtype pair; LMHEAD_OK when the call may proceed.
+lmhead_status check_call(int64_t M, int64_t H, int64_t V, int in_dtype, int out_dtype, int path) {
+  lmhead_status st = check_shape(M, H, V);
+  if (st != LMHEAD_OK) return st;
+  if (!known_dtype(in_dtype) || !known_dtype(out_dtype)) return LMHEAD_ERR_INVALID;
+  if (path != LMHEAD_PATH_AUTO && path != LMHEAD_PATH_SKINNY && path != LMHEAD_PATH_TILED)
+    return LMHEAD_ERR_INVALID;
+  // 16-bit inputs of one type; logits fp32 or of the input type
+  if (in_dtype == LMHEAD_F32 || (out_dtype != LMHEAD_F32 && out_dtype != in_dtype))
+    return LMHEAD_NOT_HANDLED;
+  return LMHEAD_OK;
+}
+
+// Launches the GEMM with its epilogue writing the logits (out) and / or the
+// row-reduction partials (part); arguments already checked.
+hipError_t run_gemm(const void *hidden, int64_t M, int64_t H, const void *W, int64_t V,
+                    float alpha, const float *bias, lmhead_dtype in_dtype, lmhead_dtype out_dtype,
+                    void *out, void *part, hipStream_t s, int path) {
+  lmhead::GemmArgs a;
+  a.hidden = static_cast<const uint16_t *>(hidden);
+  a.M = M;
+  a.H = H;
+  a.W = static_cast<const uint16_t *>(W);
+  a.V = V;
+  a.alpha = alpha;
+  a.bias = bias;
+  a.in_f16 = in_dtype == LMHEAD_F16 ? 1 : 0;
+  a.out_type = out_dtype == LMHEAD_F32    ? lmhead::OUT_F32
+               : out_dtype == LMHEAD_BF16 ? lmhead::OUT_BF16
+                                          : lmhead::OUT_F16;
+  a.out = out;
+  a.part = part;
+  const int p = path == LMHEAD_PATH_AUTO ? auto_path(M) : path;
+  return p == LMHEAD_PATH_SKINNY ? lmhead::launch_skinny(a, s) : lmhead::launch_tiled(a, s);
+}
+
+int64_t part_bytes(int64_t M, int64_t V) { return 16 * M * ((V + 15) / 16); }
+
 }  // namespace
 
 namespace lmhead {
@@ -90,36 +129,45 @@ const char *lmhead_version(void) { return "0.1.0"; }
 lmhead_status lmhead_logits_ex(const void *hidden, int64_t M, int64_t H, const void *W, int64_t V,
                                float alpha, const float *bias, lmhead_dtype in_dtype,
                                lmhead_dtype out_dtype, void *out, void *stream, int path) {
-  lmhead_status st = check_shape(M, H, V);
+  lmhead_status st = check_call(M, H, V, in_dtype, out_dtype, path);
   if (st != LMHEAD_OK) return st;
-  if (!known_dtype(in_dtype) || !known_dtype(out_dtype)) return LMHEAD_ERR_INVALID;
-  if (path != LMHEAD_PATH_AUTO && path != LMHEAD_PATH_SKINNY && path != LMHEAD_PATH_TILED)
-    return LMHEAD_ERR_INVALID;
-  // 16-bit inputs of one type; logits fp32 or of the input type
-  if (in_dtype == LMHEAD_F32 || (out_dtype != LMHEAD_F32 && out_dtype != in_dtype))
-    return LMHEAD_NOT_HANDLED;
   if (M == 0) return LMHEAD_OK;  // nothing to do, nothing launched
   if (hidden == nullptr || W == nullptr || out == nullptr) return LMHEAD_ERR_INVALID;
   if (!aligned(hidden, 16) || !aligned(W, 16) || !aligned(out, 16) ||
       (bias != nullptr && !aligned(bias, 4)))
     return LMHEAD_ERR_ALIGN;
+  hipError_t e = run_gemm(hidden, M, H, W, V, alpha, bias, in_dtype, out_dtype, out, nullptr,
+                          static_cast<hipStream_t>(stream), path);
+  return e == hipSuccess ? LMHEAD_OK : LMHEAD_ERR_DEVICE;
+}
 
-  lmhead::GemmArgs a;
-  a.hidden = static_cast<const uint16_t *>(hidden);
-  a.M = M;
-  a.H = H;
-  a.W = static_cast<const uint16_t *>(W);
-  a.V = V;
-  a.alpha = alpha;
-  a.bias = bias;
-  a.in_f16 = in_dtype == LMHEAD_F16 ? 1 : 0;
-  a.out_type = out_dtype == LMHEAD_F32    ? lmhead::OUT_F32
-               : out_dtype == LMHEAD_BF16 ? lmhead::OUT_BF16
-                                          : lmhead::OUT_F16;
-  a.out = out;
-  const int p = path == LMHEAD_PATH_AUTO ? auto_path(M) : path;
+size_t lmhead_rowreduce_workspace_bytes(int64_t M, int64_t V) {
+  if (check_shape(M, 32, V) == LMHEAD_ERR_INVALID) return 0;
+  return (size_t)part_bytes(M, V);
+}
+
+lmhead_status lmhead_logits_rowreduce(const void *hidden, int64_t M, int64_t H, const void *W,
+                                      int64_t V, float alpha, const float *bias,
+                                      lmhead_dtype in_dtype, lmhead_dtype out_dtype, void *out,
+                                      float *row_max, int32_t *row_argmax, float *row_sumexp,
+                                      void *workspace, size_t workspace_bytes, void *stream,
+                                      int path) {
+  lmhead_status st = check_call(M, H, V, in_dtype, out_dtype, path);
+  if (st != LMHEAD_OK) return st;
+  if (M == 0) return LMHEAD_OK;
+  if (hidden == nullptr || W == nullptr || row_max == nullptr || row_argmax == nullptr ||
+      row_sumexp == nullptr || workspace == nullptr)
+    return LMHEAD_ERR_INVALID;
+  if (workspace_bytes < (size_t)part_bytes(M, V)) return LMHEAD_ERR_INVALID;
+  if (!aligned(hidden, 16) || !aligned(W, 16) || (out != nullptr && !aligned(out, 16)) ||
+      !aligned(workspace, 16) || !aligned(row_max, 4) || !aligned(row_argmax, 4) ||
+      !aligned(row_sumexp, 4) || (bias != nullptr && !aligned(bias, 4)))
+    return LMHEAD_ERR_ALIGN;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  hipError_t e = p == LMHEAD_PATH_SKINNY ? lmhead::launch_skinny(a, s) : lmhead::launch_tiled(a, s);
+  hipError_t e = run_gemm(hidden, M, H, W, V, alpha, bias, in_dtype, out_dtype, out, workspace,
+                          s, path);
+  if (e == hipSuccess) e = lmhead::launch_row_combine(workspace, M, V, row_max, row_argmax,
+                                                      row_sumexp, s);
   return e == hipSuccess ? LMHEAD_OK : LMHEAD_ERR_DEVICE;
 }
 

@@ -86,7 +86,8 @@ typedef __attribute__((address_space(3))) void sk_lds_void;
 template <int R, int NB, bool DMA, bool F16, typename OutT>
 __global__ __launch_bounds__(SK_THREADS, SK_WAVES >= 8 ? 1 : 2) void skinny_kernel(
     const uint16_t *__restrict__ hidden, int64_t M, int64_t H, const uint16_t *__restrict__ W,
-    int64_t V, float alpha, const float *__restrict__ bias, OutT *__restrict__ out) {
+    int64_t V, float alpha, const float *__restrict__ bias, OutT *__restrict__ out,
+    RowPart *__restrict__ part) {
   constexpr int ROWS = 16 * R;
   constexpr int HPC = ROWS * SK_CPR;                           // hidden pieces per chunk
   constexpr int HL = (HPC + SK_THREADS - 1) / SK_THREADS;      // ... per thread
@@ -162,6 +163,15 @@ __global__ __launch_bounds__(SK_THREADS, SK_WAVES >= 8 ? 1 : 2) void skinny_kern
   for (int j = 0; j < NB; ++j)
 #pragma unroll
     for (int r = 0; r < R; ++r) acc[j][r] = zero4();
+
+  // The wave's logits and / or row-reduction partials (acc is indexed
+  // [column block][row block]).
+  auto epilogue_all = [&](f32x4 (&a)[NB][R]) {
+    const int64_t rows = M - m0 < 16 * R ? M - m0 : 16 * R;
+    auto at = [&](int i, int j) -> f32x4 & { return a[j][i]; };
+    if (out != nullptr) store_blocks<R, NB>(at, out, m0, rows, cb0 * 16, cend, V, alpha, bias);
+    if (part != nullptr) reduce_blocks<R, NB>(at, part, m0, rows, cb0 * 16, cend, V, alpha, bias);
+  };
 
   u32x4 wb[SK_P][NB];
   auto load_w = [&](int slot, int64_t step) {
@@ -266,8 +276,7 @@ __global__ __launch_bounds__(SK_THREADS, SK_WAVES >= 8 ? 1 : 2) void skinny_kern
     }
     if (c < nst) kstep_dma((int)(c & 1), 0, (c & 1) ? Wl1 : Wl0);  // H % 64 == 32
     if (!active) return;
-    store_blocks<R, NB>([&](int i, int j) -> f32x4 & { return acc[j][i]; }, out, m0,
-                        M - m0 < 16 * R ? M - m0 : 16 * R, cb0 * 16, cend, V, alpha, bias);
+    epilogue_all(acc);
     return;
   }
 
@@ -302,9 +311,7 @@ __global__ __launch_bounds__(SK_THREADS, SK_WAVES >= 8 ? 1 : 2) void skinny_kern
   }
 
   if (!active) return;
-  // acc is indexed [column block][row block]
-  store_blocks<R, NB>([&](int i, int j) -> f32x4 & { return acc[j][i]; }, out, m0,
-                      M - m0 < 16 * R ? M - m0 : 16 * R, cb0 * 16, cend, V, alpha, bias);
+  epilogue_all(acc);
 }
 
 template <int R, int NB, bool F16, typename OutT>
@@ -312,7 +319,8 @@ hipError_t launch_nb(const GemmArgs &a, int64_t nvs, hipStream_t stream) {
   dim3 grid((unsigned)(nvs * ((a.M + 63) / 64)));
   constexpr bool DMA = NB <= 2;
   return launch_kernel(skinny_kernel<R, NB, DMA, F16, OutT>, grid, dim3(SK_THREADS), stream,
-                       a.hidden, a.M, a.H, a.W, a.V, a.alpha, a.bias, static_cast<OutT *>(a.out));
+                       a.hidden, a.M, a.H, a.W, a.V, a.alpha, a.bias, static_cast<OutT *>(a.out),
+                       static_cast<RowPart *>(a.part));
 }
 
 // The variant with NB = the split's blocks per wave (NB <= NBM).

@@ -65,7 +65,8 @@ struct TiledArgs {
   int64_t V;
   float alpha;             // epilogue scale (NVFP4: fl32(global_scale * alpha))
   const float *bias;       // [V] or nullptr
-  void *out;               // [M, V]
+  void *out;               // [M, V], or nullptr
+  void *part;              // row-reduction partials [M, ceil(V / 16)], or nullptr
 };
 
 // WM x WN waves; each owns a (TM / WM) x (TN / WN) sub-tile of at most 4 x 8
@@ -77,7 +78,11 @@ struct TiledArgs {
 // loads it one stage ahead into registers, and at the stage's turn decodes it
 // (exact bf16, nvfp4_decode.hpp) into the same swizzled LDS layout the direct
 // loads fill. Every weight element is decoded once per tile, whatever M.
-template <int TM, int TN, int WM, int WN, bool NV, bool F16, typename OutT>
+//
+// RED: the epilogue also writes the row-reduction partials (args.part); a
+// separate instantiation, so the plain kernel's register allocation does not
+// carry the reduction's code.
+template <int TM, int TN, int WM, int WN, bool NV, bool F16, typename OutT, bool RED>
 __global__ __launch_bounds__(64 * WM * WN, 1) void tiled_kernel(TiledArgs args) {
   const uint16_t *__restrict__ hidden = args.hidden;
   const int64_t M = args.M, H = args.H, V = args.V;
@@ -248,14 +253,24 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void tiled_kernel(TiledArgs args) 
   }
 
   const int64_t rb = m0 + wm * SM;
-  store_blocks<FM, FN>([&](int i, int j) -> f32x4 & { return acc[i][j]; }, out, rb,
-                       M - rb < SM ? M - rb : SM, n0 + wn * SN, V, V, alpha, bias);
+  const int64_t rows = M - rb < SM ? M - rb : SM;
+  auto at = [&](int i, int j) -> f32x4 & { return acc[i][j]; };
+  if (!RED || out != nullptr)
+    store_blocks<FM, FN>(at, out, rb, rows, n0 + wn * SN, V, V, alpha, bias);
+  if constexpr (RED)
+    reduce_blocks<FM, FN>(at, static_cast<RowPart *>(args.part), rb, rows, n0 + wn * SN, V, V,
+                          alpha, bias);
 }
 
 template <int TM, int TN, int WM, int WN, bool NV, bool F16, typename OutT>
 hipError_t launch_tm(const TiledArgs &a, hipStream_t stream) {
   const int64_t tiles = ((a.M + TM - 1) / TM) * ((a.V + TN - 1) / TN);
-  return launch_kernel(tiled_kernel<TM, TN, WM, WN, NV, F16, OutT>, dim3((unsigned)tiles),
+  if constexpr (!NV) {
+    if (a.part != nullptr)
+      return launch_kernel(tiled_kernel<TM, TN, WM, WN, NV, F16, OutT, true>,
+                           dim3((unsigned)tiles), dim3(64 * WM * WN), stream, a);
+  }
+  return launch_kernel(tiled_kernel<TM, TN, WM, WN, NV, F16, OutT, false>, dim3((unsigned)tiles),
                        dim3(64 * WM * WN), stream, a);
 }
 
@@ -277,7 +292,7 @@ hipError_t launch_t(const TiledArgs &a, hipStream_t stream) {
 }  // namespace
 
 hipError_t launch_tiled(const GemmArgs &a, hipStream_t stream) {
-  const TiledArgs t{a.hidden, a.M, a.H, a.W, nullptr, nullptr, a.V, a.alpha, a.bias, a.out};
+  const TiledArgs t{a.hidden, a.M, a.H, a.W, nullptr, nullptr, a.V, a.alpha, a.bias, a.out, a.part};
   if (a.in_f16)
     return a.out_type == OUT_F32 ? launch_t<true, float>(t, stream)
                                  : launch_t<true, _Float16>(t, stream);
@@ -286,7 +301,8 @@ hipError_t launch_tiled(const GemmArgs &a, hipStream_t stream) {
 }
 
 hipError_t launch_tiled_nvfp4(const Nvfp4Args &a, hipStream_t stream) {
-  const TiledArgs t{a.hidden, a.M, a.H, nullptr, a.codes, a.scales, a.V, a.scale, a.bias, a.out};
+  const TiledArgs t{a.hidden, a.M, a.H, nullptr, a.codes, a.scales, a.V, a.scale, a.bias, a.out,
+                    nullptr};
   // 128 x 128 tiles of four waves: measured 12% faster at M = 256 than
   // 256 x 256 or 128 x 256 tiles (more tiles in flight per CU; the decode of
   // each weight tile is repeated once per 128 rows of M).

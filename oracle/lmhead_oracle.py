@@ -39,6 +39,11 @@ Readings where the pages are silent (each listed in the design notes):
   definition; each fp16 x fp16 product is exact in binary64. fp32 output as
   above; fp16 output: alpha*S (+ b) correctly rounded to binary16, with
   gradual underflow and overflow to infinity.
+* Row reduction (the fused epilogue of the library's row-reduction entry
+  point): over a row's fp32 logits, the maximum, the lowest column holding it
+  (ties keep the lowest index, as a stable descending sort does -- tokenspeed
+  PR 720, summary and review thread) and sum exp(x - max) in binary64, the
+  pieces of the softmax that drives acceptance (vLLM PR 49120, Purpose).
 * NVFP4 layout: codes [V, H/2] row-major, element 2i in the low nibble of byte
   i and 2i+1 in the high nibble; one OCP E4M3 scale per 16 consecutive
   elements of a weight row, [V, H/16] row-major; one fp32 per-tensor scale g.
@@ -54,7 +59,9 @@ E2M1 magnitudes of the OCP MX specification, one-hot weights (a gather) and
 zero hidden rows (bias only); for fp16, a hand-computed example (tests/golden),
 binary16 decoding against numpy's float16 for every bit pattern, binary16
 rounding against exact rational rounding, rational brute force and integer
-inputs past bf16's range against numpy's int64 matmul.
+inputs past bf16's range against numpy's int64 matmul; for the row reduction,
+a hand example with ties (tests/golden), scipy's logsumexp on random rows,
+exact shift and reversal invariants and closed forms (constant rows).
 """
 from __future__ import annotations
 
@@ -293,3 +300,35 @@ def lmhead_logits_nvfp4(h_bits, packed, scale_bytes, g: float, alpha: float = 1.
     if bias is not None:
         y = y + np.asarray(bias, dtype=np.float32).astype(np.float64)
     return f64_to_bf16_correct(y), A
+
+
+# ----------------------------------------------------------------------------
+# Row reduction of the logits.
+# ----------------------------------------------------------------------------
+
+
+def row_reduce(x):
+    """Softmax quantities of each row of fp32 logits x [M, V]:
+    (max, argmax, sumexp) with max the largest value (fp32), argmax the lowest
+    column holding it (numpy's argmax returns the first occurrence), and
+    sumexp = sum_v exp(x[m, v] - max) in binary64, so that the row's
+    log-sum-exp is max + log(sumexp).
+
+    Greedy selection with ties going to the lowest index is the stable
+    descending order of tokenspeed PR 720 (summary and review thread); the
+    softmax of the logits is the acceptance distribution of vLLM PR 49120
+    (section Purpose)."""
+    x = np.asarray(x, dtype=np.float32)
+    idx = np.argmax(x, axis=1)
+    mx = x[np.arange(x.shape[0]), idx]
+    s = np.exp(x.astype(np.float64) - mx.astype(np.float64)[:, None]).sum(axis=1)
+    return mx, idx.astype(np.int64), s
+
+
+def lmhead_rowreduce(h_bits, w_bits, alpha: float, bias=None, in_dtype: str = "bf16"):
+    """Row reduction of the fp32 logits of ``lmhead_logits``: returns
+    (max, argmax, sumexp, logits, A)."""
+    S, A = dot_f64(h_bits, w_bits, in_dtype)
+    x = logits_f32(S, alpha, bias)
+    mx, idx, s = row_reduce(x)
+    return mx, idx, s, x, A

@@ -136,3 +136,70 @@ def check_f16(gpu_bits, ref_bits, A, scale, ulp_fn, rel=2e-5, what=""):
         raise AssertionError(f"{what}: {int(bad.sum())} fp16 elements out of tolerance, e.g. "
                              + ", ".join(f"gpu={g[i]!r} ref={r[i]!r}" for i in idx))
     return int(np.sum(err > ulp))
+
+
+# ---------------------------------------------------------------------------
+# Row reduction.
+# ---------------------------------------------------------------------------
+
+U32 = 2.0 ** -24   # unit roundoff of binary32
+
+
+def sumexp_bound(x, m, V):
+    """Bound on |s_gpu - sum_v exp(x_v - m)| for a row reduced at fp32 from its
+    fp32 logits x with maximum m, in the library's fixed order. Each
+    exponential is 2^(d log2 e) for a rounded difference d: the difference,
+    the product and the hardware exp2 (taken as within 2 ulp) give a relative
+    error of at most 3u|d| + 4u. A term exp(x_v - m) is the block's
+    exp(x_v - m_b) rescaled by factors exp(m_prev - m_next) whose differences
+    add up to m_b - m, so its relative error is at most 3u|x_v - m| plus 4u
+    per level; the sum passes through at most L = 4 + ceil(ceil(V/16) / 1024)
+    + 6 + 4 levels (16-lane block sum, the combine thread's folds, the 64-lane
+    and the 16-wave butterflies), each adding at most 4u more (multiply, add).
+    Returned in binary64, per row."""
+    x = np.asarray(x, dtype=np.float64)
+    m = np.asarray(m, dtype=np.float64)[:, None]
+    e = np.exp(x - m)
+    ncb = (V + 15) // 16
+    L = 4 + (ncb + 1023) // 1024 + 6 + 4
+    return (e * 3 * U32 * np.abs(x - m)).sum(axis=1) + e.sum(axis=1) * 8 * L * U32
+
+
+def check_rowreduce_self(gmax, garg, gsum, x):
+    """The GPU's row reduction against its own fp32 logits x [M, V]: max and
+    argmax exactly (the lowest column of the maximum), sumexp within
+    ``sumexp_bound``."""
+    x = np.asarray(x, dtype=np.float32)
+    idx = np.argmax(x, axis=1)
+    mx = x[np.arange(x.shape[0]), idx]
+    assert np.array_equal(np.asarray(gmax, np.float32), mx), \
+        "row max differs from the maximum of the logits"   # by value: +0 == -0
+    assert np.array_equal(np.asarray(garg, np.int64), idx), "argmax is not the lowest maximal column"
+    ref = np.exp(x.astype(np.float64) - mx.astype(np.float64)[:, None]).sum(axis=1)
+    err = np.abs(np.asarray(gsum, np.float64) - ref)
+    bound = sumexp_bound(x, mx, x.shape[1])
+    assert np.all(err <= bound), f"sumexp beyond its bound: max err/bound {np.max(err / bound):.3g}"
+    return float(np.max(err / bound))
+
+
+def check_rowreduce_oracle(gmax, garg, gsum, ref_max, ref_x, A, V, rel=2e-5):
+    """The GPU's row reduction against the oracle's. With every logit within
+    tol_v = rel*A_v + 1e-30 of the oracle's (the fp32 parity bound) and both
+    max and log-sum-exp 1-Lipschitz in the largest coordinate change, the row
+    max and log-sum-exp are within T = max_v tol_v (plus the sumexp rounding
+    for the latter); the argmax column's oracle logit is within 2T of the
+    oracle maximum."""
+    T = (rel * np.asarray(A, np.float64) + 1e-30).max(axis=1)
+    gmax = np.asarray(gmax, np.float64)
+    assert np.all(np.abs(gmax - ref_max) <= T), "row max beyond tolerance"
+    lse_gpu = gmax + np.log(np.asarray(gsum, np.float64))
+    ref_x64 = np.asarray(ref_x, np.float64)
+    ref_s = np.exp(ref_x64 - np.asarray(ref_max, np.float64)[:, None]).sum(axis=1)
+    lse_ref = np.asarray(ref_max, np.float64) + np.log(ref_s)
+    # sumexp rounding, relative, taken at the oracle's logits (within T of the GPU's)
+    srel = sumexp_bound(ref_x, ref_max, V) / ref_s
+    assert np.all(np.abs(lse_gpu - lse_ref) <= T * (1 + 1e-6) + 2 * srel + 1e-12), \
+        "log-sum-exp beyond tolerance"
+    rows = np.arange(ref_x64.shape[0])
+    assert np.all(ref_x64[rows, np.asarray(garg)] >= np.asarray(ref_max) - 2 * T), \
+        "argmax column is not within tolerance of the maximum"

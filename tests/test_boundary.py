@@ -127,3 +127,32 @@ def test_alignment():
     assert call(bias=FAKE + 2) == A
     assert call4(codes=FAKE + 8) == A
     assert call4(scales=FAKE + 1) == A
+
+
+def callr(hidden=FAKE, M=4, H=64, W=FAKE, V=100, alpha=1.0, bias=None, din=1, dout=0, out=None,
+          rmax=FAKE, rarg=FAKE, rsum=FAKE, ws=FAKE, wsb=None, path=-2):
+    wsb = 16 * M * ((V + 15) // 16) if wsb is None else wsb
+    return _lib.load().lmhead_logits_rowreduce(hidden, M, H, W, V, alpha, bias, din, dout, out,
+                                               rmax, rarg, rsum, ws, wsb, None, path)
+
+
+def test_rowreduce_workspace_size():
+    f = _lib.load().lmhead_rowreduce_workspace_bytes
+    assert f(1, 1) == 16 and f(1, 16) == 16 and f(1, 17) == 32
+    assert f(64, 128256) == 16 * 64 * 8016
+    assert f(0, 100) == 0 and f(-1, 100) == 0 and f(4, 0) == 0
+
+
+def test_rowreduce_host_checks():
+    E, A = _lib.ERR_INVALID, _lib.ERR_ALIGN
+    assert callr(M=0, hidden=None, W=None, rmax=None, rarg=None, rsum=None, ws=None) == _lib.OK
+    for k in ("hidden", "W", "rmax", "rarg", "rsum", "ws"):
+        assert callr(**{k: None}) == E, k
+    assert callr(wsb=16 * 4 * 7 - 1) == E                 # workspace one byte short
+    assert callr(ws=FAKE + 8) == A
+    assert callr(rmax=FAKE + 2) == A and callr(rarg=FAKE + 1) == A and callr(rsum=FAKE + 3) == A
+    assert callr(out=FAKE + 4) == A
+    assert callr(H=48) == _lib.NOT_HANDLED
+    assert callr(din=_lib.LMHEAD_F32) == _lib.NOT_HANDLED
+    assert callr(dout=_lib.LMHEAD_F16) == _lib.NOT_HANDLED  # bf16 inputs, fp16 logits
+    assert callr(path=_lib.PATH_NVFP4) == E

@@ -396,3 +396,56 @@ def test_integer_f16_inputs_match_int64_matmul():
         got, _ = oracle.lmhead_logits(h, w, alpha, None, "f32", in_dtype="f16")
         want = (exact.astype(np.float32) * np.float32(alpha)).astype(np.float32)
         assert np.array_equal(got, want)
+
+
+# ---------------------------------------------------------------------------
+# Row reduction (max, lowest argmax, sum of exp(x - max)).
+# ---------------------------------------------------------------------------
+
+def test_rowreduce_hand_example():
+    g = load_golden("rowreduce_hand.txt")
+    h = f32_bits_to_bf16_bits_exact(_rows(g, "hidden"))
+    w = f32_bits_to_bf16_bits_exact(_rows(g, "weight"))
+    for a in g["alpha"][0]:
+        alpha = num(a)
+        mx, idx, s, x, _ = oracle.lmhead_rowreduce(h, w, alpha)
+        want_m = np.array([num(v) for v in g[f"max_alpha{a}"][0]], dtype=np.float32)
+        assert np.array_equal(mx.view(np.uint32), want_m.view(np.uint32)), a   # -0 kept
+        assert list(idx) == [int(v) for v in g[f"argmax_alpha{a}"][0]], a
+        want_s = np.array([num(v) for v in g[f"sumexp_alpha{a}"][0]])
+        assert np.allclose(s, want_s, rtol=1e-14, atol=0), a
+
+
+def test_rowreduce_vs_scipy_logsumexp():
+    from scipy.special import logsumexp
+    rng = np.random.default_rng(21)
+    x = (rng.normal(0, 3, (50, 777))).astype(np.float32)
+    x[7] = -100.0                              # a constant row
+    x[8, [3, 400, 700]] = 50.0                 # ties far apart
+    mx, idx, s = oracle.row_reduce(x)
+    lse = mx.astype(np.float64) + np.log(s)
+    want = logsumexp(x.astype(np.float64), axis=1)
+    assert np.allclose(lse, want, rtol=1e-14, atol=1e-13)
+    assert np.array_equal(mx, x.max(axis=1))
+    assert idx[7] == 0 and s[7] == 777.0
+    assert idx[8] == 3
+    # every argmax holds the maximum, and no earlier column does
+    for r in range(x.shape[0]):
+        assert x[r, idx[r]] == mx[r] and np.all(x[r, :idx[r]] < mx[r])
+
+
+def test_rowreduce_invariants():
+    rng = np.random.default_rng(22)
+    x = rng.integers(-30, 30, (20, 300)).astype(np.float32)   # integer rows: shifts are exact
+    mx, idx, s = oracle.row_reduce(x)
+    mx2, idx2, s2 = oracle.row_reduce(x + np.float32(1024))
+    assert np.array_equal(mx2, mx + 1024) and np.array_equal(idx2, idx) and np.array_equal(s2, s)
+    # reversing a row maps the lowest argmax to the highest tied column
+    mr, ir, sr = oracle.row_reduce(x[:, ::-1])
+    last = 299 - np.array([np.flatnonzero(row == row.max())[-1] for row in x])
+    assert np.array_equal(ir, last) and np.array_equal(mr, mx)
+    assert np.allclose(sr, s, rtol=1e-13)
+    # one dominant column: sumexp -> 1
+    y = np.full((1, 100), -1000.0, np.float32)
+    y[0, 42] = 0.0
+    assert oracle.row_reduce(y)[2][0] == 1.0 and oracle.row_reduce(y)[1][0] == 42
