@@ -7,8 +7,9 @@ one lmhead_logits call for each M in {1, 2, 8, 32, 64}. The headline value is
 the whole step's algorithmic HBM throughput (weight read once + hidden +
 output written, divided by the step time). The other workloads -- prefill
 (M=2048), spec-decode (M=128 with bias), the NVFP4 head (M in 1, 16, 64,
-256), fp16 inputs (M in 1, 64, 2048) and the row-reduction epilogue (decode
-M = 64, spec M = 128) -- are timed after it and reported alongside.
+256), fp16 inputs (M in 1, 64, 2048), the row-reduction epilogue (decode
+M = 64, spec M = 128) and the BF16 -> NVFP4 quantiser -- are timed after it
+and reported alongside.
 
 Inputs are generated on the host from the seeded generator, copied to HBM
 before timing, and never touched by the timed region. Timing uses HIP events
@@ -262,6 +263,24 @@ def bench_rowreduce(torch, L, wl, dev, warmup, steps):
     return res
 
 
+def bench_quantize(torch, L, wl, dev, warmup, steps):
+    """BF16 -> NVFP4 quantisation of the NVFP4 workload's head (V = 151936,
+    H = 2048, 622 MB of bf16): the absmax pass reads the weight once, the
+    quantiser reads it again and writes 9/16 byte per element."""
+    w = wl.NVFP4
+    log("quantize: generating inputs")
+    Wd = to_dev_bf16(torch, wl.bf16_head(w), dev)
+    ws = torch.empty(1 << 16, dtype=torch.uint8, device=dev)
+    _, _, per = timed_calls(torch, [lambda: L.quantize_nvfp4(Wd, workspace=ws)], warmup, steps)
+    us = 1e3 * float(np.mean(per[0]))
+    n = w.V * w.H
+    by = 2 * n * 2 + n // 2 + n // 16
+    del Wd
+    return {"V": w.V, "H": w.H, "us_avg": round(us, 1), "GBps": round(by / us / 1e3, 1),
+            "frac_hbm": round(by / us / 1e3 / HBM_PEAK_GBPS, 4),
+            "algorithmic_bytes": by, "roofline_us": round(by / HBM_PEAK_GBPS / 1e3, 1)}
+
+
 def bench_copy(torch, dev, warmup, steps, nbytes=1 << 30):
     """A plain device-to-device copy of `nbytes` (torch's copy kernel): reads
     and writes exactly nbytes, so the HBM counters read on it give the scale
@@ -317,7 +336,7 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--only", choices=["decode", "prefill", "spec", "nvfp4", "f16", "rowreduce",
-                                       "copy", "all"],
+                                       "quantize", "copy", "all"],
                     default="all",
                     help="run one workload only (for profiling; 'copy' is the HBM counter "
                          "calibration); the headline line needs decode")
@@ -343,6 +362,7 @@ def main():
               "nvfp4": lambda: bench_nvfp4(torch, L, wl, dev, args.warmup, args.steps),
               "f16": lambda: bench_f16(torch, L, wl, dev, args.warmup, args.steps),
               "rowreduce": lambda: bench_rowreduce(torch, L, wl, dev, args.warmup, args.steps),
+              "quantize": lambda: bench_quantize(torch, L, wl, dev, args.warmup, args.steps),
               "copy": lambda: bench_copy(torch, dev, args.warmup, args.steps)}[args.only]
         print(json.dumps({"workload": args.only, "result": fn()}), flush=True)
         return
@@ -361,6 +381,9 @@ def main():
         torch.cuda.empty_cache()
     if run("rowreduce"):
         extra["rowreduce"] = bench_rowreduce(torch, L, wl, dev, args.warmup, args.steps)
+        torch.cuda.empty_cache()
+    if run("quantize"):
+        extra["quantize_nvfp4"] = bench_quantize(torch, L, wl, dev, args.warmup, args.steps)
 
     w = dec["w"]
     step_ms = dec["step_ms"]

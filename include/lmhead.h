@@ -188,6 +188,33 @@ lmhead_status lmhead_logits_nvfp4(const void *hidden, int64_t M, int64_t H,
                                   float global_scale, int64_t V, float alpha, const float *bias,
                                   void *out, void *stream);
 
+/* BF16 -> NVFP4 quantisation of a head: the weight lmhead_logits_nvfp4 reads,
+ * made from a bf16 weight in two passes -- the tensor's absolute maximum, then
+ * block quantisation -- as the metrale page "layers/mtp_head/new_bf16_moe.rs"
+ * requantises BF16 weights to NVFP4 at load with an absmax kernel and an NVFP4
+ * kernel (quantize_to_nvfp4, new_nvfp4_draft_moe). Every step is a binary32
+ * operation (division correctly rounded):
+ *   g = amax / 2688 (6 * 448; 1 when that is 0), amax = max |W|
+ *   per 16 consecutive elements of a row: s = bmax / (6 g) rounded to E4M3
+ *     (nearest even, at most 448); d = e4m3(s) * g
+ *   per element: code = sign bit of W | E2M1(|W| / d) (nearest even,
+ *     at most 6; magnitude 0 when d == 0)
+ *   W             bf16 [V, H], finite               (device, read)
+ *   w_e2m1        uint8 [V, H/2], layout as in lmhead_logits_nvfp4 (device, written)
+ *   w_scale       uint8 [V, H/16]                   (device, written)
+ *   global_scale  one fp32, g                       (device, written)
+ *   workspace     at least lmhead_quantize_nvfp4_workspace_bytes() bytes of
+ *                 device memory, 4-byte aligned, overwritten by the call
+ * Shape contract as for the projection with M = 1 (H % 32 != 0:
+ * LMHEAD_NOT_HANDLED). Alignment: W 16, w_e2m1 4, global_scale 4 bytes.
+ * The result is deterministic (maxima are exact, the per-element steps fixed). */
+lmhead_status lmhead_quantize_nvfp4(const void *W, int64_t V, int64_t H, uint8_t *w_e2m1,
+                                    uint8_t *w_scale, float *global_scale, void *workspace,
+                                    size_t workspace_bytes, void *stream);
+
+/* Host-only: bytes of workspace lmhead_quantize_nvfp4 needs (a constant). */
+size_t lmhead_quantize_nvfp4_workspace_bytes(void);
+
 /* Host-only shape predicate (no device access): 1 when (M, H, V) is inside the
  * shape contract of the bf16 (nvfp4 = 0) or NVFP4 (nvfp4 = 1) entry point,
  * else 0. Like the shape check the metrale page's install step runs before

@@ -16,7 +16,8 @@ from . import _lib
 from ._lib import (LMHEAD_BF16, LMHEAD_F16, LMHEAD_F32, NOT_HANDLED, OK, PATH_AUTO, PATH_NONE,
                    PATH_NVFP4, PATH_SKINNY, PATH_TILED)
 
-__all__ = ["logits", "logits_rowreduce", "rowreduce_workspace_bytes", "logits_nvfp4", "shape_ok", "path_for", "status_string", "version",
+__all__ = ["logits", "logits_rowreduce", "rowreduce_workspace_bytes", "logits_nvfp4",
+           "quantize_nvfp4", "shape_ok", "path_for", "status_string", "version",
            "LmHeadError", "NotHandled", "PATH_SKINNY", "PATH_TILED", "PATH_NVFP4", "PATH_AUTO",
            "PATH_NONE"]
 
@@ -160,6 +161,31 @@ def logits_rowreduce(hidden: torch.Tensor, weight: torch.Tensor, alpha: float = 
             _PATHS[path])
     _check(st, "lmhead_logits_rowreduce")
     return row_max, row_argmax, row_sumexp, out
+
+
+def quantize_nvfp4(weight: torch.Tensor, *, workspace: torch.Tensor | None = None, stream=None):
+    """BF16 [V, H] -> NVFP4 (lmhead_quantize_nvfp4): returns (codes uint8
+    [V, H/2], scales uint8 [V, H/16], global_scale fp32 [1]), all on the
+    weight's device; logits_nvfp4 takes float(global_scale)."""
+    _need(weight.is_cuda and weight.dtype == torch.bfloat16 and weight.dim() == 2
+          and weight.is_contiguous(), "weight must be a contiguous bf16 [V, H] device tensor")
+    V, H = weight.shape
+    dev = weight.device
+    codes = torch.empty((V, H // 2), dtype=torch.uint8, device=dev)
+    scales = torch.empty((V, H // 16), dtype=torch.uint8, device=dev)
+    g = torch.empty(1, dtype=torch.float32, device=dev)
+    need = int(_lib.load().lmhead_quantize_nvfp4_workspace_bytes())
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    _need(workspace.is_cuda and workspace.is_contiguous(), "workspace must be a contiguous device tensor")
+    _same_device(weight, workspace)
+    with torch.cuda.device(dev):
+        st = _lib.load().lmhead_quantize_nvfp4(
+            weight.data_ptr(), V, H, codes.data_ptr(), scales.data_ptr(), g.data_ptr(),
+            workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+            _stream_handle(dev, stream))
+    _check(st, "lmhead_quantize_nvfp4")
+    return codes, scales, g
 
 
 def logits_nvfp4(hidden: torch.Tensor, codes: torch.Tensor, scales: torch.Tensor,

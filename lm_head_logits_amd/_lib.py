@@ -27,7 +27,8 @@ PATH_TILED = 1
 PATH_NVFP4 = 2
 
 EXPORTS = ("lmhead_logits", "lmhead_logits_path", "lmhead_logits_ex", "lmhead_logits_rowreduce",
-           "lmhead_rowreduce_workspace_bytes", "lmhead_logits_nvfp4", "lmhead_shape_ok",
+           "lmhead_rowreduce_workspace_bytes", "lmhead_logits_nvfp4", "lmhead_quantize_nvfp4",
+           "lmhead_quantize_nvfp4_workspace_bytes", "lmhead_shape_ok",
            "lmhead_path_for", "lmhead_status_string", "lmhead_version")
 
 _lib = None
@@ -57,6 +58,10 @@ def load() -> ctypes.CDLL:
                                             vp, vp, ctypes.c_size_t, vp, i32]
     lib.lmhead_rowreduce_workspace_bytes.restype = ctypes.c_size_t
     lib.lmhead_rowreduce_workspace_bytes.argtypes = [i64, i64]
+    lib.lmhead_quantize_nvfp4.restype = i32
+    lib.lmhead_quantize_nvfp4.argtypes = [vp, i64, i64, vp, vp, vp, vp, ctypes.c_size_t, vp]
+    lib.lmhead_quantize_nvfp4_workspace_bytes.restype = ctypes.c_size_t
+    lib.lmhead_quantize_nvfp4_workspace_bytes.argtypes = []
     lib.lmhead_logits_nvfp4.restype = i32
     lib.lmhead_logits_nvfp4.argtypes = [vp, i64, i64, vp, vp, f32, i64, f32, vp, vp, vp]
     lib.lmhead_shape_ok.restype = i32

@@ -69,6 +69,12 @@ VSplit vsplit(int64_t ncb, int waves, int nb_max);
 hipError_t launch_row_combine(const void *part, int64_t M, int64_t V, float *row_max,
                               int32_t *row_argmax, float *row_sumexp, hipStream_t stream);
 
+// BF16 -> NVFP4 quantisation of a [V, H] head (two kernels); the workspace
+// holds the absmax pass's partial maxima.
+size_t quantize_nvfp4_workspace_bytes();
+hipError_t launch_quantize_nvfp4(const uint16_t *W, int64_t V, int64_t H, uint8_t *codes,
+                                 uint8_t *scales, float *g, void *workspace, hipStream_t stream);
+
 hipError_t launch_skinny(const GemmArgs &a, hipStream_t stream);
 hipError_t launch_tiled(const GemmArgs &a, hipStream_t stream);
 hipError_t launch_nvfp4(const Nvfp4Args &a, hipStream_t stream);

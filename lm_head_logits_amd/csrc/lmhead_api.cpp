@@ -190,6 +190,26 @@ lmhead_status lmhead_logits(const void *hidden, int64_t M, int64_t H, const void
                             LMHEAD_PATH_AUTO);
 }
 
+size_t lmhead_quantize_nvfp4_workspace_bytes(void) { return lmhead::quantize_nvfp4_workspace_bytes(); }
+
+lmhead_status lmhead_quantize_nvfp4(const void *W, int64_t V, int64_t H, uint8_t *w_e2m1,
+                                    uint8_t *w_scale, float *global_scale, void *workspace,
+                                    size_t workspace_bytes, void *stream) {
+  lmhead_status st = check_shape(1, H, V);
+  if (st != LMHEAD_OK) return st;
+  if (W == nullptr || w_e2m1 == nullptr || w_scale == nullptr || global_scale == nullptr ||
+      workspace == nullptr)
+    return LMHEAD_ERR_INVALID;
+  if (workspace_bytes < lmhead::quantize_nvfp4_workspace_bytes()) return LMHEAD_ERR_INVALID;
+  if (!aligned(W, 16) || !aligned(w_e2m1, 4) || !aligned(global_scale, 4) ||
+      !aligned(workspace, 4))
+    return LMHEAD_ERR_ALIGN;
+  hipError_t e = lmhead::launch_quantize_nvfp4(static_cast<const uint16_t *>(W), V, H, w_e2m1,
+                                               w_scale, global_scale, workspace,
+                                               static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? LMHEAD_OK : LMHEAD_ERR_DEVICE;
+}
+
 lmhead_status lmhead_logits_nvfp4(const void *hidden, int64_t M, int64_t H,
                                   const uint8_t *w_e2m1, const uint8_t *w_scale,
                                   float global_scale, int64_t V, float alpha, const float *bias,

@@ -44,6 +44,12 @@ Readings where the pages are silent (each listed in the design notes):
   (ties keep the lowest index, as a stable descending sort does -- tokenspeed
   PR 720, summary and review thread) and sum exp(x - max) in binary64, the
   pieces of the softmax that drives acceptance (vLLM PR 49120, Purpose).
+* BF16 -> NVFP4 quantisation (two passes, as the metrale mtp_head page's
+  quantize_to_nvfp4 runs an absmax kernel and an NVFP4 kernel): the pages
+  give no arithmetic; the reading is the two-level recipe g = amax / (6*448),
+  block scale E4M3_RNE(bmax / (6 g)), codes E2M1_RNE(|w| / (scale * g)),
+  every step a binary32 operation (the decisions are integers, so both sides
+  take them in the same precision).
 * NVFP4 layout: codes [V, H/2] row-major, element 2i in the low nibble of byte
   i and 2i+1 in the high nibble; one OCP E4M3 scale per 16 consecutive
   elements of a weight row, [V, H/16] row-major; one fp32 per-tensor scale g.
@@ -332,3 +338,85 @@ def lmhead_rowreduce(h_bits, w_bits, alpha: float, bias=None, in_dtype: str = "b
     x = logits_f32(S, alpha, bias)
     mx, idx, s = row_reduce(x)
     return mx, idx, s, x, A
+
+
+# ----------------------------------------------------------------------------
+# BF16 -> NVFP4 quantisation of a head (the step before the NVFP4 projection).
+# ----------------------------------------------------------------------------
+
+E2M1_MAX = 6.0
+E4M3_MAX = 448.0
+
+
+def f32_to_e4m3_rne(s) -> np.ndarray:
+    """Non-negative binary32 values -> OCP E4M3 bytes, round to nearest even,
+    saturating at 448 (0x7E). |s| lies in the binade [2^e, 2^(e+1)) with
+    e >= -6 (the subnormals share the spacing of the lowest binade), where
+    E4M3 keeps 4 significant bits: spacing 2^(e-3)."""
+    s = np.asarray(s, dtype=np.float32).astype(np.float64)    # exact widening
+    assert np.all(s >= 0)
+    _, fe = np.frexp(s)
+    e = np.maximum(fe - 1, -6)
+    n = np.rint(np.ldexp(s, 3 - e))                            # nearest even, in [0, 16]
+    carry = n >= 16
+    e = np.where(carry, e + 1, e)
+    n = np.where(carry, 8, n).astype(np.int64)
+    sub = n < 8                                                # only at e == -6
+    field = np.where(sub, 0, e + 7)
+    code = np.where(sub, n, (field << 3) | (n - 8))
+    over = (field > 15) | ((field == 15) & (n - 8 == 7)) | (s >= E4M3_MAX)
+    return np.where(over, 0x7E, code).astype(np.uint8)
+
+
+def e2m1_rne(x) -> np.ndarray:
+    """Non-negative binary32 magnitudes -> E2M1 magnitude codes 0..7 (values 0,
+    0.5, 1, 1.5, 2, 3, 4, 6), nearest with ties to the even code (the one
+    whose mantissa bit is 0), saturating at 6."""
+    x = np.asarray(x, dtype=np.float64)
+    grid = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
+    d = np.abs(x[..., None] - grid)                            # distance to each value
+    best = d.min(axis=-1, keepdims=True)
+    cand = d == best                                           # one, or two at a tie
+    even = (np.arange(8) % 2) == 0
+    pick = np.where(cand & even, np.arange(8), 99).min(axis=-1)
+    pick = np.where(cand.sum(axis=-1) == 1, np.argmax(cand, axis=-1), pick)
+    return np.where(x >= E2M1_MAX, 7, pick).astype(np.uint8)
+
+
+def quantize_nvfp4(w_bits, amax=None):
+    """BF16 weight [V, H] (H % 16 == 0) -> (codes [V, H/2] u8, scales [V, H/16]
+    u8, g fp32), every step an IEEE binary32 operation:
+
+      amax = max |w|;  g = fl32(amax / 2688), or 1 when that is 0
+      per block of 16:  s = fl32(bmax / fl32(6 g)),  byte = E4M3_RNE_sat(s),
+                        d = fl32(e4m3(byte) * g)
+      per element:      code = sign bit of w | E2M1_RNE_sat(fl32(|w| / d)), or
+                        the sign bit alone when d == 0
+
+    Two passes over the weight -- a per-tensor absolute maximum, then block
+    quantisation -- as the metrale page's quantize_to_nvfp4 runs an absmax
+    kernel and then an NVFP4 kernel (mtp_head/new_bf16_moe.rs source page,
+    new_nvfp4_draft_moe). The constants put the largest block scale at E4M3's
+    largest value (448) and the largest element at E2M1's (6).
+
+    `amax`, when given, is the whole tensor's maximum, for quantising a subset
+    of its rows."""
+    w = bf16_to_f64(w_bits).astype(np.float32)                 # exact
+    V, H = w.shape
+    a = np.abs(w)
+    if amax is None:
+        amax = a.max() if a.size else np.float32(0)
+    g = np.float32(amax) / np.float32(E2M1_MAX * E4M3_MAX)
+    g = np.float32(1.0) if g == 0 else np.float32(g)
+    blocks = a.reshape(V, H // 16, 16)
+    bmax = blocks.max(axis=-1)
+    s = (bmax / (np.float32(E2M1_MAX) * g)).astype(np.float32)
+    scales = f32_to_e4m3_rne(s)
+    d = (e4m3_to_f64(scales).astype(np.float32) * g).astype(np.float32)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        x = (blocks / d[..., None]).astype(np.float32)
+    mag = np.where(d[..., None] == 0, 0, e2m1_rne(np.where(d[..., None] == 0, 0, x)))
+    neg = np.signbit(w.reshape(V, H // 16, 16)).astype(np.uint8)   # -0 keeps its sign
+    code = (mag.astype(np.uint8) | (neg << 3)).reshape(V, H)
+    packed = (code[:, 0::2] | (code[:, 1::2] << 4)).astype(np.uint8)
+    return packed, scales, np.float32(g)

@@ -94,6 +94,12 @@ def weight_rows(w: Workload, v0: int, nv: int) -> np.ndarray:
     return _normal(w)(w.seed, STREAM_WEIGHT, (nv, w.H), std=W_STD, start=v0 * w.H)
 
 
+def bf16_head(w: Workload) -> np.ndarray:
+    """bf16 bits [V, H] of N(0, 0.02) at the workload's head shape: the input
+    of the BF16 -> NVFP4 quantiser."""
+    return normal_bf16(w.seed, STREAM_WEIGHT, (w.V, w.H), std=W_STD)
+
+
 def bias(w: Workload) -> np.ndarray | None:
     if not w.bias:
         return None

@@ -156,3 +156,21 @@ def test_rowreduce_host_checks():
     assert callr(din=_lib.LMHEAD_F32) == _lib.NOT_HANDLED
     assert callr(dout=_lib.LMHEAD_F16) == _lib.NOT_HANDLED  # bf16 inputs, fp16 logits
     assert callr(path=_lib.PATH_NVFP4) == E
+
+
+def callq(W=FAKE, V=100, H=64, codes=FAKE, scales=FAKE, g=FAKE, ws=FAKE, wsb=None):
+    lib = _lib.load()
+    wsb = lib.lmhead_quantize_nvfp4_workspace_bytes() if wsb is None else wsb
+    return lib.lmhead_quantize_nvfp4(W, V, H, codes, scales, g, ws, wsb, None)
+
+
+def test_quantize_host_checks():
+    E, A = _lib.ERR_INVALID, _lib.ERR_ALIGN
+    assert _lib.load().lmhead_quantize_nvfp4_workspace_bytes() >= 4
+    for k in ("W", "codes", "scales", "g", "ws"):
+        assert callq(**{k: None}) == E, k
+    assert callq(wsb=3) == E
+    assert callq(V=0) == E and callq(H=0) == E and callq(V=(1 << 20) + 1) == E
+    assert callq(H=48) == _lib.NOT_HANDLED
+    assert callq(W=FAKE + 8) == A and callq(codes=FAKE + 2) == A and callq(g=FAKE + 2) == A
+    assert callq(ws=FAKE + 2) == A

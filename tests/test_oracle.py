@@ -449,3 +449,84 @@ def test_rowreduce_invariants():
     y = np.full((1, 100), -1000.0, np.float32)
     y[0, 42] = 0.0
     assert oracle.row_reduce(y)[2][0] == 1.0 and oracle.row_reduce(y)[1][0] == 42
+
+
+# ---------------------------------------------------------------------------
+# BF16 -> NVFP4 quantisation.
+# ---------------------------------------------------------------------------
+
+def test_quantize_hand_example():
+    g = load_golden("nvfp4_quant_hand.txt")
+    w = f32_bits_to_bf16_bits_exact(_rows(g, "weight"))
+    codes, scales, gs = oracle.quantize_nvfp4(w)
+    assert gs == np.float32(num(g["g"][0][0]))
+    assert list(scales[0]) == [int(x, 16) for x in g["scales"][0]]
+    assert list(codes[0]) == [int(x, 16) for x in g["codes"][0]]
+
+
+def test_e4m3_encoder_vs_torch():
+    rng = np.random.default_rng(31)
+    x = np.concatenate([rng.uniform(0, 448, 20000), np.exp2(rng.uniform(-12, 8.8, 20000)),
+                        # exact ties between neighbouring E4M3 values
+                        (oracle.e4m3_to_f64(np.arange(0, 126)) + oracle.e4m3_to_f64(np.arange(1, 127))) / 2
+                        ]).astype(np.float32)
+    x = x[x <= 448]
+    want = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(oracle.f32_to_e4m3_rne(x), want)
+    assert oracle.f32_to_e4m3_rne(np.float32(1e6)) == 0x7E        # saturates
+
+
+def test_e2m1_rounding_thresholds():
+    # The same rounding written as thresholds: the midpoints between
+    # neighbouring E2M1 values, a tie going to the code whose mantissa bit is 0.
+    rng = np.random.default_rng(32)
+    mids = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0])
+    x = np.concatenate([rng.uniform(0, 8, 50000), mids, np.nextafter(mids, 0), np.nextafter(mids, 9),
+                        [0.0, 6.0, 1e9]]).astype(np.float32)
+    up_at_tie = np.array([False, True, False, True, False, True, False])   # tie -> the upper code is even
+    want = sum(np.where(u, x >= m, x > m) for m, u in zip(mids, up_at_tie))
+    assert np.array_equal(oracle.e2m1_rne(x), want.astype(np.uint8))
+
+
+def _exact_nvfp4_head(rng, V, H, k):
+    """A bf16 head whose every block is exactly e2m1 x e4m3 x g with g = 2^-k,
+    each block holding a code-7 (6.0) element and one block scale 448: the
+    quantiser must give back these codes and scales."""
+    codes = rng.integers(0, 16, (V, H)).astype(np.uint8)
+    codes[:, ::16] = rng.choice([7, 15], (V, H // 16))        # +-6 in every block
+    scales = rng.integers(0x08, 0x7F, (V, H // 16)).astype(np.uint8)   # normal E4M3 values
+    scales[0, 0] = 0x7E
+    g = 2.0 ** -k
+    w = oracle.e2m1_to_f64(codes) * np.repeat(oracle.e4m3_to_f64(scales), 16, axis=1) * g
+    packed = (codes[:, 0::2] | (codes[:, 1::2] << 4)).astype(np.uint8)
+    return f32_bits_to_bf16_bits_exact(w), packed, scales, g
+
+
+def test_quantize_recovers_an_exact_nvfp4_head():
+    rng = np.random.default_rng(33)
+    w, packed, scales, g = _exact_nvfp4_head(rng, 7, 64, 12)
+    c2, s2, g2 = oracle.quantize_nvfp4(w)
+    assert g2 == np.float32(g) and np.array_equal(s2, scales)
+    # a code for +-0 may come back with either sign bit: compare values
+    assert np.array_equal(oracle.e2m1_to_f64(oracle.unpack_e2m1(c2, 64)),
+                          oracle.e2m1_to_f64(oracle.unpack_e2m1(packed, 64)))
+
+
+def test_quantize_scale_invariance_error_bound_and_zero():
+    rng = np.random.default_rng(34)
+    w = oracle.f32_to_bf16_rne(rng.normal(0, 0.02, (9, 96)).astype(np.float32))
+    c, s, g = oracle.quantize_nvfp4(w)
+    w2 = f32_bits_to_bf16_bits_exact(oracle.bf16_to_f64(w) * 4)      # exact
+    c2, s2, g2 = oracle.quantize_nvfp4(w2)
+    assert np.array_equal(c, c2) and np.array_equal(s, s2) and g2 == np.float32(4 * g)
+    # every element is within half an E2M1 spacing (in units of its block's
+    # scale d), or saturated at 6 when it exceeds 6 d
+    wf = oracle.bf16_to_f64(w)
+    d = np.repeat(oracle.e4m3_to_f64(s) * np.float64(g), 16, axis=1)
+    q = oracle.e2m1_to_f64(oracle.unpack_e2m1(c, 96))
+    x = np.abs(wf) / d
+    half = np.where(x < 2, 0.25, np.where(x < 4, 0.5, 1.0)) * (1 + 1e-6)
+    assert np.all((np.abs(np.abs(q) - x) <= half) | ((x > 6) & (np.abs(q) == 6)))
+    assert np.all(np.sign(q) * np.sign(wf) >= 0)
+    z, zs, zg = oracle.quantize_nvfp4(np.zeros((2, 32), np.uint16))
+    assert zg == 1.0 and not z.any() and not zs.any()
