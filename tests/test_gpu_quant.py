@@ -95,3 +95,35 @@ def test_full_nvfp4_head_and_projection():
     cols = rows
     ref, A = oracle.lmhead_logits_nvfp4(h, _np(codes)[cols], _np(scales)[cols], gs)
     check_bf16(out[:, cols], ref, A, gs, oracle.ulp_bf16, what="quantised head")
+
+
+def test_concurrent_quantisation_on_streams():
+    import threading
+    rng = np.random.default_rng(36)
+    say("quantise threads and streams")
+    heads = [bf16_dev(oracle.f32_to_bf16_rne((rng.normal(0, 0.02 * (i + 1), (700 + 97 * i, 128)))
+                                             .astype(np.float32))) for i in range(4)]
+    serial = [[_np(t) for t in L.quantize_nvfp4(h)] for h in heads]
+    torch.cuda.synchronize()
+    outs, errors = [None] * 4, []
+
+    def work(i):
+        try:
+            s = torch.cuda.Stream(device=DEV)
+            with torch.cuda.stream(s):
+                for _ in range(3):
+                    r = L.quantize_nvfp4(heads[i], stream=s)
+            s.synchronize()
+            outs[i] = [_np(t) for t in r]
+        except Exception as e:  # reported below, on the test's thread
+            errors.append(e)
+
+    threads = [threading.Thread(target=work, args=(i,)) for i in range(4)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    assert not errors, errors
+    for a, b in zip(serial, outs):
+        for x, y in zip(a, b):
+            assert np.array_equal(x, y)

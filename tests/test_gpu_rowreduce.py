@@ -159,3 +159,40 @@ def test_decode_shape_parity():
     ref_m, _, _, ref_x, A = oracle.lmhead_rowreduce(h[rows], W, alpha)
     check_rowreduce_oracle(_np(mx)[rows], _np(am)[rows], _np(se)[rows], ref_m, ref_x, A, w.V)
     say(f"  sumexp max err/bound {ratio:.3g}")
+
+
+def test_concurrent_calls_with_own_workspaces():
+    # Calls from several host threads, each on its own stream with its own
+    # workspace, give the bits of the same calls made one by one.
+    import threading
+    rng = np.random.default_rng(12)
+    say("rowreduce threads and streams")
+    hd = bf16_dev(_rand_bf16(rng, (96, 256), 1.0))
+    Wd = bf16_dev(_rand_bf16(rng, (9000, 256), 0.02))
+    Ms = [1, 7, 64, 96, 33, 65]
+    serial = [[_np(t) for t in L.logits_rowreduce(hd[:m].contiguous(), Wd, 0.25)[:3]] for m in Ms]
+    torch.cuda.synchronize()
+    outs, errors = [None] * len(Ms), []
+
+    def work(i):
+        try:
+            s = torch.cuda.Stream(device=DEV)
+            with torch.cuda.stream(s):
+                ws = torch.empty(L.rowreduce_workspace_bytes(Ms[i], 9000), dtype=torch.uint8, device=DEV)
+                h = hd[:Ms[i]].contiguous()
+                for _ in range(3):
+                    r = L.logits_rowreduce(h, Wd, 0.25, workspace=ws, stream=s)
+            s.synchronize()
+            outs[i] = [_np(t) for t in r[:3]]
+        except Exception as e:  # reported below, on the test's thread
+            errors.append(e)
+
+    threads = [threading.Thread(target=work, args=(i,)) for i in range(len(Ms))]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    assert not errors, errors
+    for a, b in zip(serial, outs):
+        for x, y in zip(a, b):
+            assert np.array_equal(x.view(np.uint32), y.view(np.uint32))
