@@ -82,6 +82,13 @@ def test_parity_and_paths_agree(M, H, V, alpha, has_bias, f16):
     ratio = check_rowreduce_self(*res["tiled"], plain)
     ref_m, _, _, ref_x, A = oracle.lmhead_rowreduce(h, W, alpha, bias, ind)
     check_rowreduce_oracle(*res["tiled"], ref_m, ref_x, A, V)
+    # 16-bit logits written alongside: the plain call's 16-bit logits, and the
+    # reduction still over the fp32 epilogue values
+    o16 = torch.float16 if f16 else torch.bfloat16
+    mx, am, se, lg = L.logits_rowreduce(hd, Wd, alpha, bd, o16, write_logits=True)
+    assert np.array_equal(host_bits(lg), host_bits(L.logits(hd, Wd, alpha, bd, o16)))
+    assert np.array_equal(_np(mx).view(np.uint32), res["tiled"][0].view(np.uint32))
+    assert np.array_equal(_np(se).view(np.uint32), res["tiled"][2].view(np.uint32))
     # without the logits: the same three results
     mx, am, se, lg = L.logits_rowreduce(hd, Wd, alpha, bd)
     assert lg is None
