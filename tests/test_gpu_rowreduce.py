@@ -203,3 +203,35 @@ def test_concurrent_calls_with_own_workspaces():
     for a, b in zip(serial, outs):
         for x, y in zip(a, b):
             assert np.array_equal(x.view(np.uint32), y.view(np.uint32))
+
+
+def test_vocabulary_shards_fold_to_the_full_row():
+    # The multi-GPU reading on one GPU: each of g vocabulary shards reduced by
+    # its own call, the g triples folded in shard order with the combine
+    # rule (larger maximum, ties to the lower global column, sums rescaled to
+    # the new maximum). Maximum and argmax equal the one-call result exactly;
+    # the sum of exponentials within the bound of its own fold order.
+    rng = np.random.default_rng(14)
+    M, H, V, g = 48, 256, 50000, 8
+    say(f"rowreduce vocabulary shards g={g}")
+    hd = bf16_dev(_rand_bf16(rng, (M, H), 1.0))
+    Wd = bf16_dev(_rand_bf16(rng, (V, H), 0.02))
+    mx, am, se, lg = L.logits_rowreduce(hd, Wd, 0.5, write_logits=True)
+    bounds = np.linspace(0, V, g + 1).astype(int)
+    m = np.full(M, -np.inf)
+    s = np.zeros(M)
+    idx = np.full(M, -1)
+    for r in range(g):
+        v0, v1 = bounds[r], bounds[r + 1]
+        pm, pa, ps, _ = L.logits_rowreduce(hd, Wd[v0:v1].contiguous(), 0.5)
+        pm, pa, ps = _np(pm).astype(np.float64), _np(pa) + v0, _np(ps).astype(np.float64)
+        take = pm > m                                  # shards come in column order: ties keep the earlier
+        new_m = np.where(take, pm, m)
+        s = np.where(s == 0, 0, s * np.exp(m - new_m)) + ps * np.exp(pm - new_m)
+        idx = np.where(take, pa, idx)
+        m = new_m
+    assert np.array_equal(m.astype(np.float32), _np(mx)) and np.array_equal(idx, _np(am))
+    x = host_f32(lg)
+    from helpers import sumexp_bound
+    ref = np.exp(x.astype(np.float64) - x.max(axis=1, keepdims=True)).sum(axis=1)
+    assert np.all(np.abs(s - ref) <= 2 * sumexp_bound(x, x.max(axis=1), V))
