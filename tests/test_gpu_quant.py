@@ -127,3 +127,18 @@ def test_concurrent_quantisation_on_streams():
     for a, b in zip(serial, outs):
         for x, y in zip(a, b):
             assert np.array_equal(x, y)
+
+
+@pytest.mark.parametrize("scale", [1e-37, 1e-30, 3e36, 1e37])
+def test_extreme_ranges_bitwise(scale):
+    # Heads whose per-tensor scale g or block scales d fall outside the range
+    # of the reciprocal shortcut (subnormal g and d at 1e-37, d past 2^120 at
+    # 3e36 and 1e37):
+    # those blocks take the division itself; codes must still match.
+    rng = np.random.default_rng(int(np.log10(scale) + 100))
+    say(f"quantise at scale {scale:g}")
+    wf = rng.normal(0, 1, (64, 96)) * scale
+    w = oracle.f32_to_bf16_rne(wf.astype(np.float32))
+    assert np.all(np.isfinite(oracle.bf16_to_f64(w)))
+    codes, scales, g = L.quantize_nvfp4(bf16_dev(w))
+    _check(w, codes, scales, g, what=f"scale {scale:g}")
