@@ -116,7 +116,7 @@ int lmhead_path_for(int64_t M, int64_t H, int64_t V, int nvfp4) {
 const char *lmhead_status_string(int status) {
   switch (status) {
     case LMHEAD_OK: return "ok";
-    case LMHEAD_NOT_HANDLED: return "not handled: shape outside the kernels' contract (caller falls back)";
+    case LMHEAD_NOT_HANDLED: return "not handled: shape or dtype outside the kernels' contract (caller falls back)";
     case LMHEAD_ERR_INVALID: return "invalid argument";
     case LMHEAD_ERR_ALIGN: return "misaligned pointer";
     case LMHEAD_ERR_DEVICE: return "HIP launch error";
