@@ -270,3 +270,54 @@ def test_nvfp4_parity_and_equals_bf16_path(M, H, V):
         for p in PATHS:
             twin = L.logits(bf16_dev(h), bf16_dev(wbits), s, bd, torch.bfloat16, path=p)
             assert np.array_equal(host_bits(got), host_bits(twin)), p
+
+
+def test_hip_graph_capture_and_replay():
+    # The entry points allocate, free and synchronise nothing, so they can be
+    # captured in a HIP graph (the decode loop of a server). Every replay,
+    # with eager work and synchronisations between replays, must give the
+    # eager results bit for bit.
+    rng = np.random.default_rng(17)
+    say("graph capture")
+    M, H, V = 40, 512, 6000
+    hd = bf16_dev(_rand_bf16(rng, (M, H), 1.0))
+    Wd = bf16_dev(_rand_bf16(rng, (V, H), 0.02))
+    bd = f32_dev(rng.normal(0, 0.1, V))
+    h2 = bf16_dev(_rand_bf16(rng, (150, H), 1.0))
+    codes = u8_dev(rng.integers(0, 256, (V, H // 2), dtype=np.uint8))
+    scales = u8_dev(rng.choice(np.r_[0x28:0x48], (V, H // 16)).astype(np.uint8))
+    ws = torch.empty(L.rowreduce_workspace_bytes(M, V), dtype=torch.uint8, device=DEV)
+    outs = {
+        "skinny": torch.empty((M, V), device=DEV),
+        "tiled": torch.empty((150, V), device=DEV),
+        "nvfp4": torch.empty((M, V), device=DEV, dtype=torch.bfloat16),
+    }
+
+    def run():
+        L.logits(hd, Wd, 0.25, bd, out=outs["skinny"])
+        L.logits(h2, Wd, 0.25, bd, out=outs["tiled"])
+        L.logits_nvfp4(hd, codes, scales, 0.01, out=outs["nvfp4"])
+        return L.logits_rowreduce(hd, Wd, 0.25, bd, workspace=ws)[:3]
+
+    eager_red = [t.clone() for t in run()]
+    eager = {k: v.clone() for k, v in outs.items()}
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream(device=DEV)
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        run()                                        # warm-up on the capture stream
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        red = run()
+    for rep in range(3):
+        for v in outs.values():
+            v.zero_()                                # eager work between replays
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for k in outs:
+            assert torch.equal(outs[k].view(torch.int16), eager[k].view(torch.int16)), (k, rep)
+        for a, b in zip(red, eager_red):
+            assert torch.equal(a.view(torch.int32), b.view(torch.int32)), rep
