@@ -248,8 +248,11 @@ def test_nvfp4_nibble_order_on_gpu():
 # M <= 64 runs the weight-streaming NVFP4 kernel, M > 64 the tiled kernel with
 # the decode in its B stage (128-row tiles: 129 and 300 leave ragged tiles;
 # H = 96 and 160 end in a half stage).
+# H = 2176 and 4096 (M <= 64) cross the streaming kernel's block-scale segment
+# of 2048 elements, which it reloads into LDS inside its K loop.
 @pytest.mark.parametrize("M,H,V", [(1, 32, 1), (4, 64, 100), (64, 256, 1000), (65, 96, 333),
-                                   (129, 160, 515), (200, 512, 2049), (300, 128, 1000)])
+                                   (129, 160, 515), (200, 512, 2049), (300, 128, 1000),
+                                   (3, 2176, 700), (33, 4096, 1500), (64, 2304, 333)])
 def test_nvfp4_parity_and_equals_bf16_path(M, H, V):
     rng = np.random.default_rng(M + H + V)
     say(f"nvfp4 M={M} H={H} V={V}")
@@ -270,6 +273,25 @@ def test_nvfp4_parity_and_equals_bf16_path(M, H, V):
         for p in PATHS:
             twin = L.logits(bf16_dev(h), bf16_dev(wbits), s, bd, torch.bfloat16, path=p)
             assert np.array_equal(host_bits(got), host_bits(twin)), p
+
+
+def test_nvfp4_misaligned_scales_take_the_generic_kernel():
+    # Scales at an address that is 2 but not 8 bytes aligned take the generic
+    # NVFP4 kernel: the same chain, the same bits as an aligned copy.
+    rng = np.random.default_rng(23)
+    M, H, V = 16, 256, 900
+    say("nvfp4 misaligned scales")
+    h = bf16_dev(_rand_bf16(rng, (M, H), 1.0))
+    codes = u8_dev(rng.integers(0, 256, (V, H // 2), dtype=np.uint8))
+    sc = rng.choice(np.r_[0x30:0x4A], (V, H // 16)).astype(np.uint8)
+    aligned = u8_dev(sc)
+    big = torch.zeros(V * (H // 16) + 16, dtype=torch.uint8, device=DEV)
+    shifted = big[2:2 + V * (H // 16)].view(V, H // 16)
+    shifted.copy_(aligned)
+    assert shifted.data_ptr() % 8 == 2
+    a = L.logits_nvfp4(h, codes, aligned, 0.01)
+    b = L.logits_nvfp4(h, codes, shifted, 0.01)
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
 
 
 def test_hip_graph_capture_and_replay():
