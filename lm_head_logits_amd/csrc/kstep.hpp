@@ -99,6 +99,16 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
+// Work-group barrier after which every wave's direct-to-LDS loads have
+// landed: waits for all of this wave's vector memory loads (vmcnt) and LDS
+// operations, then meets the other waves. A direct load's LDS write is
+// counted by vmcnt, and __syncthreads() does not necessarily wait for it:
+// this compiler emits vmcnt(0) before the barrier in some loop layouts and
+// not in others (seen in the generated code).
+__device__ __forceinline__ void dma_barrier() {
+  asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 // Keeps the compiler from moving any instruction across this point. Used
 // before a chunk's hidden rows are written to LDS: hoisting that write above
 // the chunk's MFMAs would make it wait for every load issued since the hidden
