@@ -143,7 +143,47 @@ def bench_decode(torch, L, wl, dev, warmup, steps):
                          "roofline_us": round(b / HBM_PEAK_GBPS / 1e3, 2)}
     launches_ms = float(np.sum([np.mean(ts) for ts in per]))
     return {"w": w, "per_m": per_m, "step_ms": step_ms, "wall_ms": wall_ms,
-            "bytes_per_step": tot_bytes, "launch_ms_sum": launches_ms, "h": h, "W": W}
+            "bytes_per_step": tot_bytes, "launch_ms_sum": launches_ms, "h": h, "W": W,
+            "hd": hd, "Wd": Wd}
+
+
+def bench_shard(torch, L, w, hd, Wd, warmup, steps, shards=8, copies=4):
+    """The decode head's one-GPU share when the vocabulary is split over
+    `shards` GPUs (V/8 = 16032 rows, 131 MB): `copies` distinct row ranges of
+    the decode weight in rotation, so successive calls cannot hit the 256 MB
+    MALL."""
+    vs = w.V // shards
+    res = {"V_shard": vs, "H": w.H, "copies": copies}
+    for M in (1, 64):
+        out = torch.empty((M, vs), dtype=torch.float32, device=hd.device)
+        fns = [(lambda i=i: L.logits(hd[:M], Wd[i * vs:(i + 1) * vs], w.alphas[1], None,
+                                     torch.float32, out=out)) for i in range(copies)]
+        _, _, per = timed_calls(torch, fns, warmup, steps)
+        us = 1e3 * float(np.mean(per))
+        b = bytes_bf16(M, w.H, vs, 4, False)
+        res[str(M)] = {"us_avg": round(us, 2), "GBps": round(b / us / 1e3, 1),
+                       "frac_hbm": round(b / us / 1e3 / HBM_PEAK_GBPS, 4),
+                       "roofline_us": round(b / HBM_PEAK_GBPS / 1e3, 2)}
+    return res
+
+
+def bench_probes(torch, L, dev, warmup, steps, nbytes=1 << 30, mfma_iters=15000):
+    """The practical ceilings on this part: a plain read of 1 GiB of HBM and
+    the bf16 MFMA-only probe (include/lmhead_probes.h), timed like the
+    projection (HIP events on the launch stream)."""
+    buf = torch.empty(nbytes // 2, dtype=torch.bfloat16, device=dev).normal_()
+    _, _, per = timed_calls(torch, [lambda: L.probe_hbm_read(buf)], warmup, steps)
+    ms = np.asarray(per[0])
+    fl = L.probe_mfma_bf16(mfma_iters, dev)
+    _, _, perm = timed_calls(torch, [lambda: L.probe_mfma_bf16(mfma_iters, dev)], 2,
+                             max(3, steps // 10))
+    msm = np.asarray(perm[0])
+    del buf
+    return {"hbm_read_GBps": round(nbytes / float(np.mean(ms)) / 1e6, 1),
+            "hbm_read_GBps_best": round(nbytes / float(np.min(ms)) / 1e6, 1),
+            "mfma_bf16_TFLOPs": round(fl / float(np.mean(msm)) / 1e9, 1),
+            "mfma_bf16_TFLOPs_best": round(fl / float(np.min(msm)) / 1e9, 1),
+            "read_bytes": nbytes, "mfma_flops_per_launch": fl}
 
 
 def bench_prefill(torch, L, wl, dev, warmup, steps):
@@ -323,12 +363,34 @@ def cpu_baseline(wl, h, W, budget_s=12.0):
         t_total += time.perf_counter() - t0
         reps += 1
     per_call = t_total / reps
+    # one thread, on a smaller slice: ns per multiply-add of the fp64 oracle
+    ns_mac = None
+    try:
+        from threadpoolctl import threadpool_limits
+        nv1 = max(256, nv // 16)
+        with threadpool_limits(limits=1):
+            t0 = time.perf_counter()
+            oracle.lmhead_logits(h[:M], W[:nv1], w.alphas[1], None, "f32")
+            ns_mac = (time.perf_counter() - t0) / (M * nv1 * w.H) * 1e9
+    except Exception:
+        pass
+    cpu_model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    cpu_model = ln.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
     b = nv * w.H * 2 + M * w.H * 2 + M * nv * 4
     return {"value": round(b / per_call / 1e9, 3), "unit": "GB/s", "cores": int(threads),
             "kind": "oracle",
             "sample": f"decode head M=64, first {nv} of {w.V} vocabulary rows, H={w.H}, fp32 out; "
                       f"{reps} calls, {per_call:.2f} s each (numpy fp64 oracle)",
-            "us_per_call_full_vocab_est": round(per_call * w.V / nv * 1e6, 0)}
+            "us_per_call_full_vocab_est": round(per_call * w.V / nv * 1e6, 0),
+            "cpu_model": cpu_model, "host_cpus": os.cpu_count(),
+            "ns_per_mac_1thread": None if ns_mac is None else round(ns_mac, 3)}
 
 
 def main():
@@ -337,7 +399,7 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--only", choices=["decode", "prefill", "spec", "nvfp4", "f16", "rowreduce",
-                                       "quantize", "copy", "all"],
+                                       "quantize", "copy", "probes", "all"],
                     default="all",
                     help="run one workload only (for profiling; 'copy' is the HBM counter "
                          "calibration); the headline line needs decode")
@@ -364,10 +426,16 @@ def main():
               "f16": lambda: bench_f16(torch, L, wl, dev, args.warmup, args.steps),
               "rowreduce": lambda: bench_rowreduce(torch, L, wl, dev, args.warmup, args.steps),
               "quantize": lambda: bench_quantize(torch, L, wl, dev, args.warmup, args.steps),
-              "copy": lambda: bench_copy(torch, dev, args.warmup, args.steps)}[args.only]
+              "copy": lambda: bench_copy(torch, dev, args.warmup, args.steps),
+              "probes": lambda: bench_probes(torch, L, dev, args.warmup, args.steps)}[args.only]
         print(json.dumps({"workload": args.only, "result": fn()}), flush=True)
         return
     dec = bench_decode(torch, L, wl, dev, args.warmup, args.steps)
+    if run("shard"):
+        extra["decode_shard_v8"] = bench_shard(torch, L, dec["w"], dec["hd"], dec["Wd"],
+                                               args.warmup, args.steps)
+    del dec["hd"], dec["Wd"]
+    torch.cuda.empty_cache()
     if run("prefill"):
         extra["prefill"] = bench_prefill(torch, L, wl, dev, args.warmup, max(5, args.steps // 5))
         torch.cuda.empty_cache()
@@ -385,6 +453,9 @@ def main():
         torch.cuda.empty_cache()
     if run("quantize"):
         extra["quantize_nvfp4"] = bench_quantize(torch, L, wl, dev, args.warmup, args.steps)
+        torch.cuda.empty_cache()
+    if run("probes"):
+        extra["probes"] = bench_probes(torch, L, dev, args.warmup, args.steps)
 
     w = dec["w"]
     step_ms = dec["step_ms"]
@@ -415,6 +486,14 @@ def main():
         "decode_per_M": dec["per_m"],
         **extra,
     }
+    if "probes" in extra:
+        # fractions of what this part sustains in practice (context; the
+        # roofline fractions above use the published peaks)
+        pr = extra["probes"]
+        ctx = {"decode_achieved_over_read_probe": round(achieved / pr["hbm_read_GBps"], 4)}
+        if "prefill" in extra:
+            ctx["prefill_over_mfma_probe"] = round(extra["prefill"]["TFLOPs"] / pr["mfma_bf16_TFLOPs"], 4)
+        line["vs_probes"] = ctx
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(wl, dec["h"], dec["W"])
     print(json.dumps(line), flush=True)

@@ -10,6 +10,8 @@ LMHEAD_NOT_HANDLED the caller gets ``NotHandled`` and decides what to do.
 """
 from __future__ import annotations
 
+import ctypes
+
 import torch
 
 from . import _lib
@@ -19,7 +21,7 @@ from ._lib import (LMHEAD_BF16, LMHEAD_F16, LMHEAD_F32, NOT_HANDLED, OK, PATH_AU
 __all__ = ["logits", "logits_rowreduce", "rowreduce_workspace_bytes", "logits_nvfp4",
            "quantize_nvfp4", "shape_ok", "path_for", "status_string", "version",
            "LmHeadError", "NotHandled", "PATH_SKINNY", "PATH_TILED", "PATH_NVFP4", "PATH_AUTO",
-           "PATH_NONE"]
+           "PATH_NONE", "probe_hbm_read", "probe_mfma_bf16"]
 
 
 class LmHeadError(RuntimeError):
@@ -223,3 +225,35 @@ def logits_nvfp4(hidden: torch.Tensor, codes: torch.Tensor, scales: torch.Tensor
 
 # Load the HIP library now: a missing or broken build fails the import.
 _lib.load()
+
+
+# ---------------------------------------------------------------------------
+# Measurement probes (include/lmhead_probes.h): not part of the projection.
+# ---------------------------------------------------------------------------
+
+def _probe_sink(device, dtype):
+    n = int(_lib.load().lmhead_probe_grid()) * 256
+    return torch.empty(n, dtype=dtype, device=device)
+
+
+def probe_hbm_read(buf: torch.Tensor, *, stream=None) -> int:
+    """Enqueue one read of `buf`'s bytes (a contiguous CUDA tensor, 16-byte
+    aligned, size a multiple of 16 bytes); returns the bytes read."""
+    _need(buf.is_cuda and buf.is_contiguous(), "buf must be a contiguous CUDA tensor")
+    nbytes = buf.numel() * buf.element_size()
+    sink = _probe_sink(buf.device, torch.int32)
+    st = _lib.load().lmhead_probe_hbm_read(buf.data_ptr(), nbytes, 0, sink.data_ptr(),
+                                           _stream_handle(buf.device, stream))
+    _check(st, "lmhead_probe_hbm_read")
+    return nbytes
+
+
+def probe_mfma_bf16(iters: int, device="cuda", *, stream=None) -> float:
+    """Enqueue the bf16 MFMA probe; returns the floating-point operations of the launch."""
+    dev = torch.device(device)
+    sink = _probe_sink(dev, torch.float32)
+    flops = ctypes.c_double(0.0)
+    st = _lib.load().lmhead_probe_mfma_bf16(int(iters), 0, sink.data_ptr(),
+                                            _stream_handle(dev, stream), ctypes.byref(flops))
+    _check(st, "lmhead_probe_mfma_bf16")
+    return flops.value

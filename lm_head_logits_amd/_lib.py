@@ -30,6 +30,8 @@ EXPORTS = ("lmhead_logits", "lmhead_logits_path", "lmhead_logits_ex", "lmhead_lo
            "lmhead_rowreduce_workspace_bytes", "lmhead_logits_nvfp4", "lmhead_quantize_nvfp4",
            "lmhead_quantize_nvfp4_workspace_bytes", "lmhead_shape_ok",
            "lmhead_path_for", "lmhead_status_string", "lmhead_version")
+# include/lmhead_probes.h: measurement probes (not part of the projection)
+PROBE_EXPORTS = ("lmhead_probe_grid", "lmhead_probe_hbm_read", "lmhead_probe_mfma_bf16")
 
 _lib = None
 
@@ -72,5 +74,11 @@ def load() -> ctypes.CDLL:
     lib.lmhead_status_string.argtypes = [i32]
     lib.lmhead_version.restype = ctypes.c_char_p
     lib.lmhead_version.argtypes = []
+    lib.lmhead_probe_grid.restype = i64
+    lib.lmhead_probe_grid.argtypes = []
+    lib.lmhead_probe_hbm_read.restype = i32
+    lib.lmhead_probe_hbm_read.argtypes = [vp, ctypes.c_size_t, i32, vp, vp]
+    lib.lmhead_probe_mfma_bf16.restype = i32
+    lib.lmhead_probe_mfma_bf16.argtypes = [i64, i32, vp, vp, ctypes.POINTER(ctypes.c_double)]
     _lib = lib
     return lib

@@ -11,21 +11,38 @@ from lm_head_logits_amd import _lib
 from helpers import ROOT
 
 HEADER = ROOT / "include" / "lmhead.h"
+PROBE_HEADER = ROOT / "include" / "lmhead_probes.h"
 
 
-def declared_functions():
-    text = re.sub(r"/\*.*?\*/", "", HEADER.read_text(), flags=re.S)
+def declared_functions(header=HEADER):
+    text = re.sub(r"/\*.*?\*/", "", header.read_text(), flags=re.S)
     return sorted(set(re.findall(r"\b(lmhead_\w+)\s*\(", text)))
 
 
 def test_header_declares_the_python_exports():
     assert declared_functions() == sorted(_lib.EXPORTS)
+    assert declared_functions(PROBE_HEADER) == sorted(_lib.PROBE_EXPORTS)
+
+
+def test_every_header_is_checked():
+    assert sorted(p.name for p in (ROOT / "include").glob("*.h")) == ["lmhead.h", "lmhead_probes.h"]
 
 
 def test_library_exports_every_declared_symbol():
     lib = ctypes.CDLL(str(_lib.lib_path()))
-    for name in declared_functions():
+    for name in declared_functions() + declared_functions(PROBE_HEADER):
         assert hasattr(lib, name), name
+
+
+def test_probes_reject_bad_arguments_on_the_host():
+    lib = _lib.load()
+    sink = ctypes.c_void_p(16)  # never dereferenced: every call below fails its host checks
+    assert lib.lmhead_probe_hbm_read(None, 1024, 0, sink, None) == _lib.ERR_INVALID
+    assert lib.lmhead_probe_hbm_read(ctypes.c_void_p(256), 1000, 0, sink, None) == _lib.ERR_INVALID
+    assert lib.lmhead_probe_hbm_read(ctypes.c_void_p(8), 1024, 0, sink, None) == _lib.ERR_INVALID
+    assert lib.lmhead_probe_hbm_read(ctypes.c_void_p(256), 1024, 0, None, None) == _lib.ERR_INVALID
+    assert lib.lmhead_probe_mfma_bf16(0, 0, sink, None, None) == _lib.ERR_INVALID
+    assert lib.lmhead_probe_mfma_bf16(10, 0, None, None, None) == _lib.ERR_INVALID
 
 
 def test_status_strings_and_version():
