@@ -5,10 +5,10 @@
 // traffic, which the bf16 x bf16 -> fp32 path cuts to one read of the bf16
 // weight). Each wave owns NB column blocks of 16 vocabulary rows and walks the
 // full H for them, its weight loads running ahead of their use: by
-// direct-to-LDS loads of 8 rows x 128 bytes, two stages of two K-steps in
-// flight, when the work-group's blocks fit in LDS (NB <= 2); else by register
-// loads of 16 bytes per lane and K-step straight into the MFMA B operand,
-// P K-steps ahead. The hidden rows (<= 64) are staged through LDS in
+// direct-to-LDS loads of 8 rows x 128 bytes into a ring of stage buffers of
+// two K-steps each, when the work-group's blocks fit in LDS (NB <= 2); else
+// by register loads of 16 bytes per lane and K-step straight into the MFMA B
+// operand, P K-steps ahead. The hidden rows (<= 64) are staged through LDS in
 // KC-element K chunks, double-buffered, so the waves of a work-group read
 // them from L2 once. The K-step chain is the one of kstep.hpp, so the results
 // equal the tiled GEMM's bit for bit.
@@ -27,8 +27,15 @@
 // Measured: the stream's bandwidth follows the number of CUs streaming, and a
 // CU that holds two work-groups while others hold one finishes last (at
 // V = 151936: 297 work-groups of 32 blocks took 1.4x as long as 238 of 40).
+// With few blocks per CU (a small vocabulary, or one GPU's share of a
+// vocabulary-sharded head) the work-group has 4 or 8 waves of one block and
+// an 8-stage ring, or 16 waves with 4 stages: sixteen waves with two stages
+// left most waves idle and too few bytes in flight (V = 16032: 28 against
+// 52 µs per call; V = 32000: 52 against 57 µs).
 // Grid (1-D): vocabulary slices times 64-row blocks of M (one for M <= 64;
 // the forced-path test drives more).
+#include <type_traits>
+
 #include "kstep.hpp"
 #include "launch.hpp"
 
@@ -43,7 +50,6 @@ namespace {
 #define LMHEAD_SK_KC 64
 #endif
 constexpr int SK_WAVES = LMHEAD_SK_WAVES;
-constexpr int SK_THREADS = 64 * SK_WAVES;
 constexpr int SK_KC = LMHEAD_SK_KC;     // K elements per LDS chunk of hidden (one barrier each)
 constexpr int SK_SPC = SK_KC / KSTEP;   // K-steps per chunk
 constexpr int SK_CPR = SK_KC / 8;       // 16-byte pieces per hidden row per chunk
@@ -76,6 +82,16 @@ __device__ __forceinline__ int wslot(int row, int p) { return row * 8 + (p ^ ((r
 
 typedef __attribute__((address_space(3))) void sk_lds_void;
 
+// Calls f(std::integral_constant<int, 0>{}) ... f(integral_constant<N - 1>)
+// in order: loops whose index must be a compile-time constant.
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F &&f) {
+  if constexpr (N > 0) {
+    static_for<N - 1>(f);
+    f(std::integral_constant<int, N - 1>{});
+  }
+}
+
 // DMA: the weight goes to LDS by direct-to-LDS buffer loads of 8 rows x 128
 // bytes (two K-steps of 8 rows) per instruction, two stages per wave in
 // flight, and reaches the MFMA through ds_read. Otherwise each lane loads its
@@ -83,20 +99,32 @@ typedef __attribute__((address_space(3))) void sk_lds_void;
 // read each weight row 128 contiguous bytes at a time (measured 2-4% faster
 // at the decode shape) but need 4 KB of LDS per column block, so they are
 // used while the work-group's blocks fit (NB <= 2).
-template <int R, int NB, bool DMA, bool F16, typename OutT>
-__global__ __launch_bounds__(SK_THREADS, SK_WAVES >= 8 ? 1 : 2) void skinny_kernel(
+//
+// NW waves per work-group and, with direct loads, NS stage buffers per wave
+// (NS - 1 stages in flight while one is read). Sixteen waves with two stages
+// serve vocabularies of more than 8 column blocks per CU; below that most of
+// sixteen waves would own no block and the few that do would keep too few
+// bytes in flight, so four waves with eight stages (up to 4 blocks per CU) or
+// eight waves with four stages (up to 8) keep about 64 KB per CU in flight.
+template <int R, int NB, bool DMA, bool F16, typename OutT, int NW = SK_WAVES, int NS = 2>
+__global__ __launch_bounds__(64 * NW, NW >= 8 ? 1 : 2) void skinny_kernel(
     const uint16_t *__restrict__ hidden, int64_t M, int64_t H, const uint16_t *__restrict__ W,
     int64_t V, float alpha, const float *__restrict__ bias, OutT *__restrict__ out,
     RowPart *__restrict__ part) {
+  constexpr int THREADS = 64 * NW;
   constexpr int ROWS = 16 * R;
   constexpr int HPC = ROWS * SK_CPR;                           // hidden pieces per chunk
-  constexpr int HL = (HPC + SK_THREADS - 1) / SK_THREADS;      // ... per thread
+  constexpr int HL = (HPC + THREADS - 1) / THREADS;            // ... per thread
   static_assert(!DMA || SK_KC == 64, "a direct-load stage is one 64-element hidden chunk");
-  constexpr int WLDS = DMA ? SK_WAVES * NB * 128 : 1;          // 16-byte slots per stage buffer
+  static_assert(NS == 2 || NS == 4 || NS == 8, "stage ring of 2, 4 or 8");
+  static_assert(DMA || NS == 2, "the register path keeps its own prefetch ring");
+  constexpr int WLDS = DMA ? NW * NB * 128 : 1;                // 16-byte slots per stage buffer
   __shared__ u32x4 hs[2][ROWS * SK_CPR];
-  // Two separately declared stage buffers, so the compiler tells the stage
-  // being loaded from the one being read (and waits for the right loads).
-  __shared__ u32x4 Wl0[WLDS], Wl1[WLDS];
+  // Separately declared stage buffers, so the compiler tells the stage being
+  // loaded from the ones being read (and waits for the right loads).
+  __shared__ u32x4 Wl0[WLDS], Wl1[WLDS], Wl2[NS > 2 ? WLDS : 1], Wl3[NS > 2 ? WLDS : 1],
+      Wl4[NS > 4 ? WLDS : 1], Wl5[NS > 4 ? WLDS : 1], Wl6[NS > 4 ? WLDS : 1],
+      Wl7[NS > 4 ? WLDS : 1];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -108,8 +136,8 @@ __global__ __launch_bounds__(SK_THREADS, SK_WAVES >= 8 ? 1 : 2) void skinny_kern
   // This wave's column blocks [cb0, cb1): the ncb blocks split evenly over
   // all waves of the grid along V, at most NB each (the host sized NB so).
   const int64_t ncb = (V + 15) / 16;
-  const int64_t tw = (int64_t)(gridDim.x / nmb) * SK_WAVES;
-  const int64_t g = ((int64_t)blockIdx.x / nmb) * SK_WAVES + wave;
+  const int64_t tw = (int64_t)(gridDim.x / nmb) * NW;
+  const int64_t g = ((int64_t)blockIdx.x / nmb) * NW + wave;
   const int64_t cb0 = g * ncb / tw, cb1 = (g + 1) * ncb / tw;
   const bool active = cb1 > cb0;  // wave-uniform
   const int64_t cend = cb1 * 16 < V ? cb1 * 16 : V;  // end of this wave's columns
@@ -131,7 +159,7 @@ __global__ __launch_bounds__(SK_THREADS, SK_WAVES >= 8 ? 1 : 2) void skinny_kern
 #pragma unroll
   for (int i = 0; i < HL; ++i) {
     // threads past the chunk's last piece re-stage the last piece (same bytes, same slot)
-    const int idx = i * SK_THREADS + tid < HPC ? i * SK_THREADS + tid : HPC - 1;
+    const int idx = i * THREADS + tid < HPC ? i * THREADS + tid : HPC - 1;
     const int row = idx / SK_CPR, ch = idx % SK_CPR;
     hvoff[i] = (uint32_t)((row * H + 8 * ch) * 2);
     hsl[i] = hslot(row, ch);
@@ -142,21 +170,23 @@ __global__ __launch_bounds__(SK_THREADS, SK_WAVES >= 8 ? 1 : 2) void skinny_kern
   const int64_t hpieces = H / 8;
   const int64_t nchunks = (nk + SK_SPC - 1) / SK_SPC;
 
-  u32x4 hreg[HL];
-  auto load_hidden = [&](int64_t c) {
+  auto load_hidden_into = [&](u32x4 (&dst)[HL], int64_t c) {
     const uint32_t soff = (uint32_t)(c * SK_KC * 2);
 #pragma unroll
     for (int i = 0; i < HL; ++i) {
       // a piece past the row end (H % 256 != 0) gets an offset past the
       // resource (2^31 + soff cannot wrap), which reads zero without a branch
       const uint32_t v = (c * SK_CPR + hch[i] < hpieces) ? hvoff[i] : 0x80000000u;
-      hreg[i] = load16(hr, v, soff);
+      dst[i] = load16(hr, v, soff);
     }
   };
-  auto store_hidden = [&](int buf) {
+  auto store_hidden_from = [&](const u32x4 (&src)[HL], int buf) {
 #pragma unroll
-    for (int i = 0; i < HL; ++i) hs[buf][hsl[i]] = hreg[i];
+    for (int i = 0; i < HL; ++i) hs[buf][hsl[i]] = src[i];
   };
+  u32x4 hreg[HL];
+  auto load_hidden = [&](int64_t c) { load_hidden_into(hreg, c); };
+  auto store_hidden = [&](int buf) { store_hidden_from(hreg, buf); };
 
   f32x4 acc[NB][R];
 #pragma unroll
@@ -207,6 +237,18 @@ __global__ __launch_bounds__(SK_THREADS, SK_WAVES >= 8 ? 1 : 2) void skinny_kern
       lvoff[h] = (uint32_t)(((lane / 8) * H + 8 * piece) * 2);
     }
     const int64_t nst = (nk + 1) / 2;  // stages of two K-steps (the last may hold one)
+    // stage buffer J of the ring (compile-time J)
+    auto wbuf = [&](auto jc) -> u32x4 * {
+      constexpr int J = decltype(jc)::value;
+      if constexpr (J == 0) return Wl0;
+      else if constexpr (J == 1) return Wl1;
+      else if constexpr (J == 2) return Wl2;
+      else if constexpr (J == 3) return Wl3;
+      else if constexpr (J == 4) return Wl4;
+      else if constexpr (J == 5) return Wl5;
+      else if constexpr (J == 6) return Wl6;
+      else return Wl7;
+    };
     auto dma_stage = [&](int64_t st, u32x4 *wl) {
       const uint32_t soff = (uint32_t)(st * 128);
       // The buffer was just read by this wave's ds_reads, and a direct load
@@ -221,12 +263,18 @@ __global__ __launch_bounds__(SK_THREADS, SK_WAVES >= 8 ? 1 : 2) void skinny_kern
               wr, (sk_lds_void *)&wl[(wave * NB + j) * 128 + 64 * h], 16, lvoff[h],
               soff + j * wjstride + (uint32_t)(h * 8 * H * 2), 0, 0);
     };
+    // Hidden chunks come through a ring of NS register sets, loaded NS chunks
+    // ahead like the weight stages: a chunk's hidden loads are issued right
+    // after the same chunk's weight loads, so the in-order wait for them
+    // (before they are stored to LDS, one chunk ahead of use) never waits for
+    // a weight stage earlier than that stage is needed.
+    u32x4 hring[NS][HL];
     // Before the first read of a stage buffer: wait for its direct loads.
-    // Issued after them, at most the other buffer's loads (2 NB) and one
-    // hidden chunk's loads (HL) may still be in flight. The compiler's own
-    // wait placement once let a read of the second block slip ahead of its
-    // load (single-chunk path, NB = 2), so the wait is explicit, fenced.
-    constexpr int VM_AFTER = 2 * NB + HL;
+    // Issued after them: that chunk's hidden loads (HL), then NS - 1 chunks
+    // of weight (2 NB) and hidden (HL) loads. The compiler's own wait
+    // placement once let a read of the second block slip ahead of its load
+    // (single-chunk path, NB = 2), so the wait is explicit, fenced.
+    constexpr int VM_AFTER = (NS - 1) * 2 * NB + NS * HL;
     static_assert(VM_AFTER < 64, "vmcnt field");
     constexpr int VM_WAIT = (VM_AFTER & 15) | ((VM_AFTER >> 4) << 14) | 0x70 | 0xF00;
     auto wait_stage = [&]() {
@@ -246,35 +294,42 @@ __global__ __launch_bounds__(SK_THREADS, SK_WAVES >= 8 ? 1 : 2) void skinny_kern
 #pragma unroll
         for (int r = 0; r < R; ++r) acc[j][r] = kstep<F16>(acc[j][r], a[r], b[j]);
     };
-    // One 64-element chunk (= one stage): its two K-steps, then the stage two
-    // ahead into the buffer just read, then the hidden hand-over.
-    auto chunk = [&](int64_t c, const u32x4 *wl) {
-      const int buf = (int)(c & 1);
-      kstep_dma(buf, 0, wl);
-      kstep_dma(buf, 1, wl);
-      dma_stage(c + 2 < nst ? c + 2 : nst - 1, (u32x4 *)wl);
+    // One 64-element chunk c (= one stage, in ring slot J = c % NS): its two
+    // K-steps, then stage c + NS into the buffer just read and hidden chunk
+    // c + NS into the register set just freed, with the hand-over of hidden
+    // chunk c + 1 to LDS in between.
+    auto chunk = [&](auto jc, int64_t c) {
+      constexpr int J = decltype(jc)::value;
+      constexpr int BUF = J & 1;  // == c & 1 (NS is even)
+      u32x4 *wl = wbuf(jc);
+      kstep_dma(BUF, 0, wl);
+      kstep_dma(BUF, 1, wl);
+      dma_stage(c + NS < nst ? c + NS : nst - 1, wl);
       sched_fence();
-      store_hidden(buf ^ 1);
+      store_hidden_from(hring[(J + 1) % NS], BUF ^ 1);
       lds_barrier();
-      load_hidden(c + 2 < nchunks ? c + 2 : nchunks - 1);
+      load_hidden_into(hring[J], c + NS < nchunks ? c + NS : nchunks - 1);
     };
-    load_hidden(0);
-    dma_stage(0, Wl0);
-    dma_stage(nst > 1 ? 1 : 0, Wl1);
-    store_hidden(0);
-    load_hidden(nchunks > 1 ? 1 : 0);
+    // prologue: the first NS stages and hidden chunks in flight (stage and
+    // chunk j interleaved, as in the loop), hidden chunk 0 in LDS
+    static_for<NS>([&](auto jc) {
+      constexpr int J = decltype(jc)::value;
+      dma_stage(J < nst ? J : nst - 1, wbuf(jc));
+      load_hidden_into(hring[J], J < nchunks ? J : nchunks - 1);
+    });
+    store_hidden_from(hring[0], 0);
     lds_barrier();
     const int64_t nfull = nk / 2;
     int64_t c = 0;
-    for (; c + 2 <= nfull; c += 2) {
-      chunk(c, Wl0);
-      chunk(c + 1, Wl1);
-    }
-    if (c < nfull) {
-      chunk(c, Wl0);
-      ++c;
-    }
-    if (c < nst) kstep_dma((int)(c & 1), 0, (c & 1) ? Wl1 : Wl0);  // H % 64 == 32
+    for (; c + NS <= nfull; c += NS) static_for<NS>([&](auto jc) { chunk(jc, c + decltype(jc)::value); });
+    static_for<NS>([&](auto jc) {
+      if (c + decltype(jc)::value < nfull) chunk(jc, c + decltype(jc)::value);
+    });
+    // H % 64 == 32: the last stage holds one K-step
+    if (nfull < nst)
+      static_for<NS>([&](auto jc) {
+        if (nfull % NS == decltype(jc)::value) kstep_dma((int)(nfull & 1), 0, wbuf(jc));
+      });
     if (!active) return;
     epilogue_all(acc);
     return;
@@ -314,11 +369,11 @@ __global__ __launch_bounds__(SK_THREADS, SK_WAVES >= 8 ? 1 : 2) void skinny_kern
   epilogue_all(acc);
 }
 
-template <int R, int NB, bool F16, typename OutT>
+template <int R, int NB, bool F16, typename OutT, int NW = SK_WAVES, int NS = 2>
 hipError_t launch_nb(const GemmArgs &a, int64_t nvs, hipStream_t stream) {
   dim3 grid((unsigned)(nvs * ((a.M + 63) / 64)));
   constexpr bool DMA = NB <= 2;
-  return launch_kernel(skinny_kernel<R, NB, DMA, F16, OutT>, grid, dim3(SK_THREADS), stream,
+  return launch_kernel(skinny_kernel<R, NB, DMA, F16, OutT, NW, NS>, grid, dim3(64 * NW), stream,
                        a.hidden, a.M, a.H, a.W, a.V, a.alpha, a.bias, static_cast<OutT *>(a.out),
                        static_cast<RowPart *>(a.part));
 }
@@ -334,8 +389,14 @@ hipError_t launch_split(const GemmArgs &a, const VSplit &sp, hipStream_t stream)
 
 template <int R, bool F16, typename OutT>
 hipError_t launch_r(const GemmArgs &a, hipStream_t stream) {
+  const int64_t ncb = (a.V + 15) / 16, cus = device_cus();
+  // few column blocks per CU: one block per wave, fewer waves, a deeper ring
+  // (at most 128 KB of stage buffers per work-group)
+  if (ncb <= 4 * cus) return launch_nb<R, 1, F16, OutT, 4, 8>(a, vsplit(ncb, 4, 1).nvs, stream);
+  if (ncb <= 8 * cus) return launch_nb<R, 1, F16, OutT, 8, 8>(a, vsplit(ncb, 8, 1).nvs, stream);
+  if (ncb <= 16 * cus) return launch_nb<R, 1, F16, OutT, 16, 4>(a, vsplit(ncb, 16, 1).nvs, stream);
   constexpr int NBM = sk_nb_max<R>();
-  return launch_split<R, NBM, F16, OutT>(a, vsplit((a.V + 15) / 16, SK_WAVES, NBM), stream);
+  return launch_split<R, NBM, F16, OutT>(a, vsplit(ncb, SK_WAVES, NBM), stream);
 }
 
 template <bool F16, typename OutT>
