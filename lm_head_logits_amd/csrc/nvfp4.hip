@@ -110,7 +110,6 @@ __global__ __launch_bounds__(256) void nvfp4_generic_kernel(const uint16_t *__re
 
   const u32x4 z = {0u, 0u, 0u, 0u};
   const int64_t nk = H / KSTEP;
-#pragma unroll 2
   for (int64_t s = 0; s < nk; ++s) {
     u32x4 b[NV_NB], a[R];
 #pragma unroll
