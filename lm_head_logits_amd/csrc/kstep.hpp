@@ -220,6 +220,79 @@ __device__ __forceinline__ void store_blocks(Acc &&acc, OutT *out, int64_t rbase
   }
 }
 
+// Bits of the 16-bit output types (round to nearest even).
+template <typename OutT>
+__device__ __forceinline__ uint16_t out_bits16(float t);
+template <>
+__device__ __forceinline__ uint16_t out_bits16<uint16_t>(float t) { return bf16_rne(t); }
+template <>
+__device__ __forceinline__ uint16_t out_bits16<_Float16>(float t) {
+  return __builtin_bit_cast(uint16_t, (_Float16)t);
+}
+
+// Floats of LDS one wave needs for store_rows_lds with FN column blocks.
+template <int FN>
+constexpr int stage_rows_floats() { return 16 * (16 * FN + 4); }
+
+// The epilogue of one wave's output through LDS, for whole rows in 16-byte
+// stores. Block-row i (16 rows x 16 FN columns) goes to the wave-private LDS
+// area `stg` row by row (row stride 16 FN + 4 floats: the four 4-row groups
+// of a block write distinct banks), is read back along its rows and written
+// with 16-byte buffer stores, so the bytes of a row leave as full cache lines
+// instead of one 64-byte (fp32) or 32-byte (16-bit) piece per store and row.
+// The values are those store_blocks writes. Requires: columns
+// [cbase, cbase + 16 FN) all inside the output (the caller checks), V % 8 == 0
+// (16-byte aligned rows), `stg` 16-byte aligned with
+// stage_rows_floats<FN>() floats. Rows from `rows` on are dropped.
+template <int FM, int FN, typename OutT, typename Acc>
+__device__ __forceinline__ void store_rows_lds(Acc &&acc, OutT *out, float *stg, int64_t rbase,
+                                               int64_t rows, int64_t cbase, int64_t V,
+                                               float alpha, const float *__restrict__ bias) {
+  constexpr int SN = 16 * FN, STR = SN + 4;
+  constexpr bool F32 = sizeof(OutT) == 4;
+  constexpr int EPS = F32 ? 4 : 8;        // elements per 16-byte store
+  constexpr int SPR = SN / EPS;           // stores per row
+  constexpr int NITEM = 16 * SPR;         // stores per block-row
+  static_assert(SN % EPS == 0, "whole 16-byte stores per row");
+  const int lane = threadIdx.x & 63;
+  const int li = lane & 15, lg = lane >> 4;
+  const rsrc_t r = make_rsrc(rows > 0 ? out + rbase * V + cbase : out,
+                             rows > 0 ? (uint32_t)(((rows - 1) * V + SN) * sizeof(OutT)) : 0u);
+  const bool has_bias = bias != nullptr;
+  float b[FN];
+#pragma unroll
+  for (int j = 0; j < FN; ++j) b[j] = has_bias ? bias[cbase + 16 * j + li] : 0.0f;
+#pragma unroll
+  for (int i = 0; i < FM; ++i) {
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        stg[(4 * lg + q) * STR + 16 * j + li] = epilogue_v(acc(i, j)[q], alpha, has_bias, b[j]);
+    __builtin_amdgcn_wave_barrier();  // other lanes' values: LDS keeps a wave's order
+#pragma unroll
+    for (int k = 0; k < (NITEM + 63) / 64; ++k) {
+      const int u = 64 * k + lane;
+      const bool ok = u < NITEM;
+      const int row = ok ? u / SPR : 0, c = u % SPR;
+      const uint32_t voff = ok ? (uint32_t)(((16 * i + row) * V + EPS * c) * sizeof(OutT)) : OFF_NONE;
+      const f32x4 *src = reinterpret_cast<const f32x4 *>(stg + row * STR + EPS * c);
+      u32x4 v;
+      if constexpr (F32) {
+        v = __builtin_bit_cast(u32x4, src[0]);
+      } else {
+        const f32x4 lo = src[0], hi = src[1];
+        v = u32x4{(uint32_t)out_bits16<OutT>(lo[0]) | ((uint32_t)out_bits16<OutT>(lo[1]) << 16),
+                  (uint32_t)out_bits16<OutT>(lo[2]) | ((uint32_t)out_bits16<OutT>(lo[3]) << 16),
+                  (uint32_t)out_bits16<OutT>(hi[0]) | ((uint32_t)out_bits16<OutT>(hi[1]) << 16),
+                  (uint32_t)out_bits16<OutT>(hi[2]) | ((uint32_t)out_bits16<OutT>(hi[3]) << 16)};
+      }
+      __builtin_amdgcn_raw_buffer_store_b128(v, r, voff, 0, STORE_POLICY);
+    }
+    __builtin_amdgcn_wave_barrier();  // reads of this block-row before the next one's writes
+  }
+}
+
 // ---------------------------------------------------------------------------
 // Row-reduction epilogue: instead of (or besides) the logits, per-row
 // partials over each 16-column block -- the block's largest logit t_max, the

@@ -266,12 +266,36 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void tiled_kernel(TiledArgs args) 
 
   const int64_t rb = m0 + wm * SM;
   const int64_t rows = M - rb < SM ? M - rb : SM;
+  const int64_t cb = n0 + wn * SN;
   auto at = [&](int i, int j) -> f32x4 & { return acc[i][j]; };
-  if (!RED || out != nullptr)
-    store_blocks<FM, FN>(at, out, rb, rows, n0 + wn * SN, V, V, alpha, bias);
+  if (!RED || out != nullptr) {
+    // Logits through LDS in whole rows (the stage buffers are free once every
+    // wave has read its last stage); waves whose columns run past V, or rows
+    // not 16-byte aligned (V % 8 != 0), store block by block.
+    constexpr int STG = stage_rows_floats<FN>();
+    constexpr int PER_A = TM * TL_PPR * 16 / (4 * STG), PER_B = TN * TL_PPR * 16 / (4 * STG);
+    static_assert(2 * PER_A + 2 * PER_B >= NW, "epilogue staging fits the stage buffers");
+    __syncthreads();
+    if (V % 8 == 0 && cb + SN <= V) {
+      int w = wave;
+      float *stg;
+      if (w < PER_A) {
+        stg = reinterpret_cast<float *>(As0) + w * STG;
+      } else if ((w -= PER_A) < PER_A) {
+        stg = reinterpret_cast<float *>(As1) + w * STG;
+      } else if ((w -= PER_A) < PER_B) {
+        stg = reinterpret_cast<float *>(Bs0) + w * STG;
+      } else {
+        w -= PER_B;
+        stg = reinterpret_cast<float *>(Bs1) + w * STG;
+      }
+      store_rows_lds<FM, FN>(at, out, stg, rb, rows, cb, V, alpha, bias);
+    } else {
+      store_blocks<FM, FN>(at, out, rb, rows, cb, V, V, alpha, bias);
+    }
+  }
   if constexpr (RED)
-    reduce_blocks<FM, FN>(at, static_cast<RowPart *>(args.part), rb, rows, n0 + wn * SN, V, V,
-                          alpha, bias);
+    reduce_blocks<FM, FN>(at, static_cast<RowPart *>(args.part), rb, rows, cb, V, V, alpha, bias);
 }
 
 template <int TM, int TN, int WM, int WN, bool NV, bool F16, typename OutT>
