@@ -82,7 +82,12 @@ struct TiledArgs {
 // RED: the epilogue also writes the row-reduction partials (args.part); a
 // separate instantiation, so the plain kernel's register allocation does not
 // carry the reduction's code.
-template <int TM, int TN, int WM, int WN, bool NV, bool F16, typename OutT, bool RED>
+//
+// TAIL: the stages left after the two-stage loop, 1 or 2 (the parity of the
+// stage count, fixed by the launch), or 0 to decide at run time. With the
+// 256 x 256 tile a run-time choice makes the compiler hold two copies of the
+// accumulators at the join and spill.
+template <int TM, int TN, int WM, int WN, bool NV, bool F16, typename OutT, bool RED, int TAIL>
 __global__ __launch_bounds__(64 * WM * WN, 1) void tiled_kernel(TiledArgs args) {
   const uint16_t *__restrict__ hidden = args.hidden;
   const int64_t M = args.M, H = args.H, V = args.V;
@@ -251,7 +256,8 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void tiled_kernel(TiledArgs args) 
   }
   // one or two stages left; the very last may hold a single K-step (H % 64 == 32)
   const bool last_full = (nsteps % 2) == 0;
-  if (kt + 1 < nstages) {
+  const bool two_left = TAIL == 0 ? kt + 1 < nstages : TAIL == 2;
+  if (two_left) {
     issue_stage(kt + 1, As1, Bs1);
     sched_fence();
     compute(As0, Bs0, 0);
@@ -298,16 +304,27 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void tiled_kernel(TiledArgs args) 
     reduce_blocks<FM, FN>(at, static_cast<RowPart *>(args.part), rb, rows, cb, V, V, alpha, bias);
 }
 
-template <int TM, int TN, int WM, int WN, bool NV, bool F16, typename OutT>
-hipError_t launch_tm(const TiledArgs &a, hipStream_t stream) {
+template <int TM, int TN, int WM, int WN, bool NV, bool F16, typename OutT, int TAIL>
+hipError_t launch_tail(const TiledArgs &a, hipStream_t stream) {
   const int64_t tiles = ((a.M + TM - 1) / TM) * ((a.V + TN - 1) / TN);
   if constexpr (!NV) {
     if (a.part != nullptr)
-      return launch_kernel(tiled_kernel<TM, TN, WM, WN, NV, F16, OutT, true>,
+      return launch_kernel(tiled_kernel<TM, TN, WM, WN, NV, F16, OutT, true, TAIL>,
                            dim3((unsigned)tiles), dim3(64 * WM * WN), stream, a);
   }
-  return launch_kernel(tiled_kernel<TM, TN, WM, WN, NV, F16, OutT, false>, dim3((unsigned)tiles),
-                       dim3(64 * WM * WN), stream, a);
+  return launch_kernel(tiled_kernel<TM, TN, WM, WN, NV, F16, OutT, false, TAIL>,
+                       dim3((unsigned)tiles), dim3(64 * WM * WN), stream, a);
+}
+
+template <int TM, int TN, int WM, int WN, bool NV, bool F16, typename OutT>
+hipError_t launch_tm(const TiledArgs &a, hipStream_t stream) {
+  if constexpr (TM == 256) {
+    const int64_t nstages = (a.H / KSTEP + 1) / 2;  // as in the kernel
+    return nstages % 2 == 0 ? launch_tail<TM, TN, WM, WN, NV, F16, OutT, 2>(a, stream)
+                            : launch_tail<TM, TN, WM, WN, NV, F16, OutT, 1>(a, stream);
+  } else {
+    return launch_tail<TM, TN, WM, WN, NV, F16, OutT, 0>(a, stream);
+  }
 }
 
 template <bool F16, typename OutT>
