@@ -14,10 +14,13 @@
 // are issued as direct-to-LDS buffer loads (buffer_load_dwordx4 ... lds, no
 // registers) before the MFMAs of stage k run, and one barrier per stage
 // (which also waits for those loads) hands the buffers over. Every output
-// element is
-// built by the K-step chain of kstep.hpp -- ascending K, one accumulator, the
-// same operand map -- so a row's bits equal the weight-streaming kernel's and
-// do not depend on M.
+// element is built by the K-step chain of kstep.hpp -- ascending K, one
+// accumulator, the same operand map -- so a row's bits equal the
+// weight-streaming kernel's and do not depend on M. After the K loop the
+// stage buffers are idle; each wave stages its logits there one 16-row block
+// at a time and writes them as whole rows with 16-byte stores
+// (store_rows_lds), which measured 6% (fp32) and 13% (bf16 logits) faster at
+// prefill than per-element stores of partial cache lines.
 //
 // LDS layout of a stage: [row][8 pieces of 16 bytes]; piece c of row r sits in
 // slot c ^ ((r >> 1) & 7), so the 16 rows one MFMA operand read touches land
