@@ -73,6 +73,17 @@ def test_prefill_parity():
     ref, A = oracle.lmhead_logits(h[rows], W[cols], alpha, None, "f32")
     ratio, exact = check_f32(got[:, cols], ref, A, what="prefill")
     say(f"  max err/bound {ratio:.3f}, bit-exact fraction {exact:.3f}")
+    hd, Wd = bf16_dev(h), bf16_dev(W)
+    # bf16 logits (whole-row stores of 16-bit values): the oracle's on the
+    # sample, and everywhere the fp32 logits rounded to nearest even
+    o16 = L.logits(hd, Wd, alpha, None, torch.bfloat16)
+    got16 = host_bits(o16[torch.as_tensor(rows, device=DEV)])[:, cols]
+    ref16, _ = oracle.lmhead_logits(h[rows], W[cols], alpha, None, "bf16")
+    check_bf16(got16, ref16, A, alpha, oracle.ulp_bf16, what="prefill bf16")
+    assert torch.equal(ibits(o16), ibits(out.to(torch.bfloat16)))
+    # rows of a shorter call (a ragged 256-row tile) equal the full call's
+    part = L.logits(hd[:300].contiguous(), Wd, alpha)
+    assert torch.equal(ibits(part), ibits(out[:300]))
 
 
 @pytest.mark.parametrize("shape", [("decode", 64, 4096, 128256), ("prefill", 2048, 4096, 151936),
