@@ -4,6 +4,8 @@ from __future__ import annotations
 import os
 import shutil
 import subprocess
+import tempfile
+from concurrent.futures import ThreadPoolExecutor
 from pathlib import Path
 
 PKG = Path(__file__).resolve().parent
@@ -12,7 +14,7 @@ LIB = PKG / "liblmhead.so"
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [
-    f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
+    f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
     "-ffp-contract=off", "-Wall",
     # no packed-fp32 VALU code: those forms are not used on this target
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
@@ -30,19 +32,36 @@ def sources():
     return sorted(CSRC.glob("*.hip")) + sorted(CSRC.glob("*.cpp"))
 
 
-def build(verbose: bool = False) -> Path:
-    """Always recompiles (a stale library must never be picked up)."""
-    tmp = LIB.with_suffix(".so.tmp")
-    cmd = [hipcc(), *HIPCC_FLAGS, "-I", str(PKG.parent / "include"), "-o", str(tmp),
-           *map(str, sources())]
-    if verbose:
-        print(" ".join(cmd), flush=True)
+def _run(cmd):
     r = subprocess.run(cmd, capture_output=True, text=True)
     # the host pass does not know the packed-fp32 feature name; that warning is expected
     noise = "is not a recognized feature for this target"
-    msgs = [l for l in (r.stdout + r.stderr).splitlines() if noise not in l]
-    if r.returncode != 0:
-        raise RuntimeError("hipcc failed:\n" + "\n".join(msgs))
+    return r.returncode, [l for l in (r.stdout + r.stderr).splitlines() if noise not in l]
+
+
+def build(verbose: bool = False) -> Path:
+    """Always recompiles (a stale library must never be picked up). Each source
+    is compiled to its own object in parallel, then the objects are linked."""
+    tmp = LIB.with_suffix(".so.tmp")
+    inc = ["-I", str(PKG.parent / "include")]
+    srcs = sources()
+    with tempfile.TemporaryDirectory(prefix="lmhead_build_") as d:
+        objs = [str(Path(d) / (s.name + ".o")) for s in srcs]
+        cmds = [[hipcc(), *HIPCC_FLAGS, *inc, "-c", str(s), "-o", o] for s, o in zip(srcs, objs)]
+        jobs = max(1, min(len(cmds), int(os.environ.get("MAX_JOBS", os.cpu_count() or 1))))
+        with ThreadPoolExecutor(jobs) as ex:
+            results = list(ex.map(_run, cmds))
+        msgs = []
+        for cmd, (rc, m) in zip(cmds, results):
+            if verbose:
+                print(" ".join(cmd), flush=True)
+            msgs += m
+            if rc != 0:
+                raise RuntimeError(f"hipcc failed on {cmd[-3]}:\n" + "\n".join(m))
+        rc, m = _run([hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", str(tmp), *objs])
+        msgs += m
+        if rc != 0:
+            raise RuntimeError("link failed:\n" + "\n".join(m))
     if verbose and msgs:
         print("\n".join(msgs))
     os.replace(tmp, LIB)
