@@ -170,6 +170,32 @@ lmhead_status lmhead_logits_rowreduce(const void *hidden, int64_t M, int64_t H, 
  * 16 * M * ceil(V / 16); 0 when M or V is outside the shape contract. */
 size_t lmhead_rowreduce_workspace_bytes(int64_t M, int64_t V);
 
+/* Bytes of the partials buffer the library holds for
+ * lmhead_logits_rowreduce_noalloc, per GPU it runs on (32 MiB). */
+#define LMHEAD_NOALLOC_SCRATCH_BYTES ((int64_t)32 << 20)
+
+/* lmhead_logits_rowreduce for callers that cannot allocate device memory:
+ * code under HIP graph capture, tight serving loops, hosts that forbid
+ * allocation. It takes no workspace: the partials go to a buffer of
+ * LMHEAD_NOALLOC_SCRATCH_BYTES that the library keeps in a file-scope device
+ * array, one per GPU, held until the process ends. The call allocates and
+ * frees nothing (no hipMalloc, no allocating library routine); the caller
+ * still passes the inputs and outputs. Arguments, results and bits are those
+ * of lmhead_logits_rowreduce with the same arguments.
+ * Limit: lmhead_rowreduce_workspace_bytes(M, V) <= LMHEAD_NOALLOC_SCRATCH_BYTES
+ * (16 M ceil(V / 16) bytes: M <= 220 rows at V = 151936), else
+ * LMHEAD_ERR_INVALID with nothing launched.
+ * Every call on one GPU shares that GPU's buffer: calls whose work overlaps in
+ * time on one GPU (other streams, other host threads) race on it and must be
+ * ordered by the caller. The buffer's device address is looked up on the
+ * first call on each device (LMHEAD_ERR_DEVICE if that fails). */
+lmhead_status lmhead_logits_rowreduce_noalloc(const void *hidden, int64_t M, int64_t H,
+                                              const void *W, int64_t V, float alpha,
+                                              const float *bias, lmhead_dtype in_dtype,
+                                              lmhead_dtype out_dtype, void *out, float *row_max,
+                                              int32_t *row_argmax, float *row_sumexp,
+                                              void *stream, int path);
+
 /* The NVFP4 W4A16 head (bf16 logits).
  *   hidden       bf16 [M, H]                    (device, read)
  *   w_e2m1       uint8 [V, H/2]: two OCP E2M1 codes per byte, element 2i in the

@@ -18,7 +18,7 @@ from . import _lib
 from ._lib import (LMHEAD_BF16, LMHEAD_F16, LMHEAD_F32, NOT_HANDLED, OK, PATH_AUTO, PATH_NONE,
                    PATH_NVFP4, PATH_SKINNY, PATH_TILED)
 
-__all__ = ["logits", "logits_rowreduce", "rowreduce_workspace_bytes", "logits_nvfp4",
+__all__ = ["logits", "logits_rowreduce", "logits_rowreduce_noalloc", "rowreduce_workspace_bytes", "logits_nvfp4",
            "quantize_nvfp4", "shape_ok", "path_for", "status_string", "version",
            "LmHeadError", "NotHandled", "PATH_SKINNY", "PATH_TILED", "PATH_NVFP4", "PATH_AUTO",
            "PATH_NONE", "probe_hbm_read", "probe_mfma_bf16"]
@@ -163,6 +163,50 @@ def logits_rowreduce(hidden: torch.Tensor, weight: torch.Tensor, alpha: float = 
             _PATHS[path])
     _check(st, "lmhead_logits_rowreduce")
     return row_max, row_argmax, row_sumexp, out
+
+
+def logits_rowreduce_noalloc(hidden: torch.Tensor, weight: torch.Tensor, alpha: float = 1.0,
+                             bias=None, out_dtype=torch.float32, out: torch.Tensor | None = None,
+                             *, row_max: torch.Tensor | None = None,
+                             row_argmax: torch.Tensor | None = None,
+                             row_sumexp: torch.Tensor | None = None, path: str = "auto",
+                             stream=None):
+    """logits_rowreduce without a workspace (lmhead_logits_rowreduce_noalloc):
+    the partials go to the library's own per-GPU buffer. With `row_max`,
+    `row_argmax`, `row_sumexp` (fp32, int32, fp32 [M]) and `out` given, this
+    allocates nothing. Returns (row_max, row_argmax, row_sumexp, out or None)."""
+    _need(hidden.is_cuda and weight.is_cuda, "hidden and weight must be device tensors")
+    _need(hidden.dtype in _DTYPES and weight.dtype in _DTYPES and out_dtype in _DTYPES,
+          "dtypes must be float32, bfloat16 or float16")
+    _need(hidden.dim() == 2 and weight.dim() == 2, "hidden [M, H] and weight [V, H] are 2-D")
+    _need(hidden.is_contiguous() and weight.is_contiguous(), "inputs must be contiguous")
+    M, H = hidden.shape
+    V, H2 = weight.shape
+    _need(H == H2, f"hidden has H={H}, weight has H={H2}")
+    in_code = _DTYPES[hidden.dtype] if hidden.dtype == weight.dtype else LMHEAD_F32
+    dev = hidden.device
+    if bias is not None:
+        _need(bias.is_cuda and bias.dtype == torch.float32 and bias.shape == (V,)
+              and bias.is_contiguous(), "bias must be a contiguous fp32 device tensor [V]")
+    if out is not None:
+        _need(out.is_cuda and out.dtype == out_dtype and out.shape == (M, V) and out.is_contiguous(),
+              "out must be a contiguous [M, V] device tensor of out_dtype")
+    outs = []
+    for t, dt in ((row_max, torch.float32), (row_argmax, torch.int32), (row_sumexp, torch.float32)):
+        if t is None:
+            t = torch.empty(M, dtype=dt, device=dev)
+        _need(t.is_cuda and t.dtype == dt and t.shape == (M,) and t.is_contiguous(),
+              f"row outputs must be contiguous [M] device tensors of {dt}")
+        outs.append(t)
+    _same_device(hidden, weight, bias, out, *outs)
+    with torch.cuda.device(dev):
+        st = _lib.load().lmhead_logits_rowreduce_noalloc(
+            hidden.data_ptr(), M, H, weight.data_ptr(), V, float(alpha),
+            bias.data_ptr() if bias is not None else None, in_code, _DTYPES[out_dtype],
+            out.data_ptr() if out is not None else None, outs[0].data_ptr(), outs[1].data_ptr(),
+            outs[2].data_ptr(), _stream_handle(dev, stream), _PATHS[path])
+    _check(st, "lmhead_logits_rowreduce_noalloc")
+    return outs[0], outs[1], outs[2], out
 
 
 def quantize_nvfp4(weight: torch.Tensor, *, workspace: torch.Tensor | None = None, stream=None):

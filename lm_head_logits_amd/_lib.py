@@ -26,8 +26,10 @@ PATH_SKINNY = 0
 PATH_TILED = 1
 PATH_NVFP4 = 2
 
+NOALLOC_SCRATCH_BYTES = 32 << 20  # LMHEAD_NOALLOC_SCRATCH_BYTES
+
 EXPORTS = ("lmhead_logits", "lmhead_logits_path", "lmhead_logits_ex", "lmhead_logits_rowreduce",
-           "lmhead_rowreduce_workspace_bytes", "lmhead_logits_nvfp4", "lmhead_quantize_nvfp4",
+           "lmhead_rowreduce_workspace_bytes", "lmhead_logits_rowreduce_noalloc", "lmhead_logits_nvfp4", "lmhead_quantize_nvfp4",
            "lmhead_quantize_nvfp4_workspace_bytes", "lmhead_shape_ok",
            "lmhead_path_for", "lmhead_status_string", "lmhead_version")
 # include/lmhead_probes.h: measurement probes (not part of the projection)
@@ -58,6 +60,9 @@ def load() -> ctypes.CDLL:
     lib.lmhead_logits_rowreduce.restype = i32
     lib.lmhead_logits_rowreduce.argtypes = [vp, i64, i64, vp, i64, f32, vp, i32, i32, vp, vp, vp,
                                             vp, vp, ctypes.c_size_t, vp, i32]
+    lib.lmhead_logits_rowreduce_noalloc.restype = i32
+    lib.lmhead_logits_rowreduce_noalloc.argtypes = [vp, i64, i64, vp, i64, f32, vp, i32, i32, vp,
+                                                    vp, vp, vp, vp, i32]
     lib.lmhead_rowreduce_workspace_bytes.restype = ctypes.c_size_t
     lib.lmhead_rowreduce_workspace_bytes.argtypes = [i64, i64]
     lib.lmhead_quantize_nvfp4.restype = i32

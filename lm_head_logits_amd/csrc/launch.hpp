@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "../../include/lmhead.h"
+
 namespace lmhead {
 
 // Element type of the logits.
@@ -74,6 +76,19 @@ hipError_t launch_row_combine(const void *part, int64_t M, int64_t V, float *row
 size_t quantize_nvfp4_workspace_bytes();
 hipError_t launch_quantize_nvfp4(const uint16_t *W, int64_t V, int64_t H, uint8_t *codes,
                                  uint8_t *scales, float *g, void *workspace, hipStream_t stream);
+
+// lmhead_logits_rowreduce in two parts, shared with the entry point that
+// takes no workspace: the host checks of everything but the workspace
+// (LMHEAD_OK also when M == 0), and the launches with a workspace of at
+// least 16 M ceil(V / 16) bytes, 16-byte aligned.
+lmhead_status rowreduce_check(const void *hidden, int64_t M, int64_t H, const void *W, int64_t V,
+                              const float *bias, int in_dtype, int out_dtype, const void *out,
+                              const float *row_max, const int32_t *row_argmax,
+                              const float *row_sumexp, int path);
+lmhead_status rowreduce_run(const void *hidden, int64_t M, int64_t H, const void *W, int64_t V,
+                            float alpha, const float *bias, int in_dtype, int out_dtype, void *out,
+                            float *row_max, int32_t *row_argmax, float *row_sumexp,
+                            void *workspace, void *stream, int path);
 
 hipError_t launch_skinny(const GemmArgs &a, hipStream_t stream);
 hipError_t launch_tiled(const GemmArgs &a, hipStream_t stream);

@@ -99,6 +99,33 @@ VSplit vsplit(int64_t ncb, int waves, int nb_max) {
   return VSplit{nvs, (int)nb};
 }
 
+lmhead_status rowreduce_check(const void *hidden, int64_t M, int64_t H, const void *W, int64_t V,
+                              const float *bias, int in_dtype, int out_dtype, const void *out,
+                              const float *row_max, const int32_t *row_argmax,
+                              const float *row_sumexp, int path) {
+  lmhead_status st = check_call(M, H, V, in_dtype, out_dtype, path);
+  if (st != LMHEAD_OK || M == 0) return st;
+  if (hidden == nullptr || W == nullptr || row_max == nullptr || row_argmax == nullptr ||
+      row_sumexp == nullptr)
+    return LMHEAD_ERR_INVALID;
+  if (!aligned(hidden, 16) || !aligned(W, 16) || (out != nullptr && !aligned(out, 16)) ||
+      !aligned(row_max, 4) || !aligned(row_argmax, 4) || !aligned(row_sumexp, 4) ||
+      (bias != nullptr && !aligned(bias, 4)))
+    return LMHEAD_ERR_ALIGN;
+  return LMHEAD_OK;
+}
+
+lmhead_status rowreduce_run(const void *hidden, int64_t M, int64_t H, const void *W, int64_t V,
+                            float alpha, const float *bias, int in_dtype, int out_dtype, void *out,
+                            float *row_max, int32_t *row_argmax, float *row_sumexp,
+                            void *workspace, void *stream, int path) {
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = run_gemm(hidden, M, H, W, V, alpha, bias, static_cast<lmhead_dtype>(in_dtype),
+                          static_cast<lmhead_dtype>(out_dtype), out, workspace, s, path);
+  if (e == hipSuccess) e = launch_row_combine(workspace, M, V, row_max, row_argmax, row_sumexp, s);
+  return e == hipSuccess ? LMHEAD_OK : LMHEAD_ERR_DEVICE;
+}
+
 }  // namespace lmhead
 
 extern "C" {
@@ -152,23 +179,13 @@ lmhead_status lmhead_logits_rowreduce(const void *hidden, int64_t M, int64_t H, 
                                       float *row_max, int32_t *row_argmax, float *row_sumexp,
                                       void *workspace, size_t workspace_bytes, void *stream,
                                       int path) {
-  lmhead_status st = check_call(M, H, V, in_dtype, out_dtype, path);
-  if (st != LMHEAD_OK) return st;
-  if (M == 0) return LMHEAD_OK;
-  if (hidden == nullptr || W == nullptr || row_max == nullptr || row_argmax == nullptr ||
-      row_sumexp == nullptr || workspace == nullptr)
-    return LMHEAD_ERR_INVALID;
-  if (workspace_bytes < (size_t)part_bytes(M, V)) return LMHEAD_ERR_INVALID;
-  if (!aligned(hidden, 16) || !aligned(W, 16) || (out != nullptr && !aligned(out, 16)) ||
-      !aligned(workspace, 16) || !aligned(row_max, 4) || !aligned(row_argmax, 4) ||
-      !aligned(row_sumexp, 4) || (bias != nullptr && !aligned(bias, 4)))
-    return LMHEAD_ERR_ALIGN;
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  hipError_t e = run_gemm(hidden, M, H, W, V, alpha, bias, in_dtype, out_dtype, out, workspace,
-                          s, path);
-  if (e == hipSuccess) e = lmhead::launch_row_combine(workspace, M, V, row_max, row_argmax,
-                                                      row_sumexp, s);
-  return e == hipSuccess ? LMHEAD_OK : LMHEAD_ERR_DEVICE;
+  lmhead_status st = lmhead::rowreduce_check(hidden, M, H, W, V, bias, in_dtype, out_dtype, out,
+                                             row_max, row_argmax, row_sumexp, path);
+  if (st != LMHEAD_OK || M == 0) return st;
+  if (workspace == nullptr || workspace_bytes < (size_t)part_bytes(M, V)) return LMHEAD_ERR_INVALID;
+  if (!aligned(workspace, 16)) return LMHEAD_ERR_ALIGN;
+  return lmhead::rowreduce_run(hidden, M, H, W, V, alpha, bias, in_dtype, out_dtype, out, row_max,
+                               row_argmax, row_sumexp, workspace, stream, path);
 }
 
 lmhead_status lmhead_logits_path(const void *hidden, int64_t M, int64_t H, const void *W,

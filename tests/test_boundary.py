@@ -191,3 +191,35 @@ def test_quantize_host_checks():
     assert callq(H=48) == _lib.NOT_HANDLED
     assert callq(W=FAKE + 8) == A and callq(codes=FAKE + 2) == A and callq(g=FAKE + 2) == A
     assert callq(ws=FAKE + 2) == A
+
+
+def calln(hidden=FAKE, M=4, H=64, W=FAKE, V=100, alpha=1.0, bias=None, din=1, dout=0, out=None,
+          rmax=FAKE, rarg=FAKE, rsum=FAKE, path=-2):
+    return _lib.load().lmhead_logits_rowreduce_noalloc(hidden, M, H, W, V, alpha, bias, din, dout,
+                                                       out, rmax, rarg, rsum, None, path)
+
+
+def test_rowreduce_noalloc_host_checks():
+    """Every rejection happens on the host, before the scratch buffer's device
+    address is looked up (no call here touches a device)."""
+    E, A = _lib.ERR_INVALID, _lib.ERR_ALIGN
+    assert calln(M=0, hidden=None, W=None, rmax=None, rarg=None, rsum=None) == _lib.OK
+    for k in ("hidden", "W", "rmax", "rarg", "rsum"):
+        assert calln(**{k: None}) == E, k
+    assert calln(rmax=FAKE + 2) == A and calln(rarg=FAKE + 1) == A and calln(rsum=FAKE + 3) == A
+    assert calln(out=FAKE + 4) == A and calln(hidden=FAKE + 8) == A
+    assert calln(H=48) == _lib.NOT_HANDLED
+    assert calln(din=_lib.LMHEAD_F32) == _lib.NOT_HANDLED
+    assert calln(path=_lib.PATH_NVFP4) == E
+    # the partials must fit the library's buffer: 16 bytes per row and 16-column block
+    cap = _lib.NOALLOC_SCRATCH_BYTES
+    V = 151936
+    per_row = 16 * ((V + 15) // 16)
+    assert calln(M=cap // per_row + 1, V=V) == E
+    assert calln(M=1, V=1 << 20, rmax=None) == E  # fits, but a NULL output is still rejected first
+
+
+def test_noalloc_scratch_constant_matches_header():
+    text = HEADER.read_text()
+    m = re.search(r"#define LMHEAD_NOALLOC_SCRATCH_BYTES \(\(int64_t\)(\d+) << (\d+)\)", text)
+    assert m and int(m.group(1)) << int(m.group(2)) == _lib.NOALLOC_SCRATCH_BYTES
