@@ -57,15 +57,15 @@ int device_cus();
 // waves of a weight-streaming kernel with `waves` waves per work-group: `nvs`
 // work-groups along V, each wave owning at most `nb` consecutive blocks. The
 // weight stream's bandwidth grows with the number of CUs streaming, so the
-// grid is one work-group per CU (fewer when V is small), with the blocks
-// spread evenly: every wave owns floor or ceil of ncb / (nvs * waves) blocks
-// (the kernels derive their own range from the grid size). Past nb_max blocks
-// per wave the grid grows instead (several work-groups per CU).
+// grid is `per_cu` work-groups per CU (fewer when V is small), with the
+// blocks spread evenly: every wave owns floor or ceil of ncb / (nvs * waves)
+// blocks (the kernels derive their own range from the grid size). Past nb_max
+// blocks per wave the grid grows instead.
 struct VSplit {
   int64_t nvs;
   int nb;
 };
-VSplit vsplit(int64_t ncb, int waves, int nb_max);
+VSplit vsplit(int64_t ncb, int waves, int nb_max, int per_cu = 1);
 
 // Folds the partials of each row into its (max, argmax, sum of exp(x - max)).
 hipError_t launch_row_combine(const void *part, int64_t M, int64_t V, float *row_max,

@@ -87,10 +87,10 @@ int device_cus() {
   return cus;
 }
 
-VSplit vsplit(int64_t ncb, int waves, int nb_max) {
-  const int64_t cus = device_cus();
+VSplit vsplit(int64_t ncb, int waves, int nb_max, int per_cu) {
+  const int64_t slots = (int64_t)device_cus() * per_cu;
   int64_t nvs = (ncb + waves - 1) / waves;  // at least one block per wave
-  if (nvs > cus) nvs = cus;
+  if (nvs > slots) nvs = slots;
   int64_t nb = (ncb + nvs * waves - 1) / (nvs * waves);
   if (nb > nb_max) {
     nb = nb_max;

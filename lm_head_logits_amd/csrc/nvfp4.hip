@@ -14,11 +14,10 @@
 // element once per 128-row tile into LDS and runs the same chain. Either way
 // the logits equal lmhead_logits on the dequantised weight with
 // alpha = fl32(g * alpha), bit for bit, so a row's bits do not depend on M.
-#include <type_traits>
-
 #include "kstep.hpp"
 #include "launch.hpp"
 #include "nvfp4_decode.hpp"
+#include "ring.hpp"
 
 namespace lmhead {
 
@@ -155,42 +154,20 @@ hipError_t launch_generic_r(const Nvfp4Args &a, hipStream_t stream) {
 }
 
 // ---------------------------------------------------------------------------
-// Streaming kernel for H % 128 == 0 (the common case): the decode-sized
+// Streaming kernels for H % 128 == 0 (the common case): the decode-sized
 // NVFP4 head at HBM speed.
-//
-// The K dimension is walked in quads of four K-steps (128 elements: 64 code
-// bytes and 8 scale bytes per weight row). Each lane loads 16 contiguous code
-// bytes -- lane group g takes the codes of the quad's K-step g for all four
-// slot groups -- so a load instruction covers 16 rows x 64 contiguous bytes.
-// A 4 x 4 transpose of 32-bit words across the four 16-lane groups (two
-// v_permlane32_swap, two v_permlane16_swap) then hands every lane the eight
-// codes of its own MFMA slots for each K-step. Dequantisation stays in
-// registers: v_cvt_scalef32_pk_f32_fp4 (scale 1.0) turns two codes into two
-// fp32 values, a multiply by the E4M3 block scale (decoded by v_cvt_f32_fp8)
-// gives the exact weight, whose upper 16 bits are its bf16 pattern. Hidden
-// rows come through LDS as in the bf16 weight-streaming kernel, eight waves
-// per work-group held in lockstep by one LDS barrier per quad.
 // ---------------------------------------------------------------------------
-#ifndef LMHEAD_NS_WAVES
-#define LMHEAD_NS_WAVES 8
-#endif
-constexpr int NS_WAVES = LMHEAD_NS_WAVES;
-constexpr int NS_THREADS = 64 * NS_WAVES;
-constexpr int NS_KC = 128;          // K per quad == K per LDS chunk of hidden
-constexpr int NS_CPR = NS_KC / 8;   // 16-byte hidden pieces per row per chunk
-#ifndef LMHEAD_NS_P
-#define LMHEAD_NS_P 2
-#endif
-constexpr int NS_P = LMHEAD_NS_P;   // quads of weight loads in flight ahead of use
-#ifndef LMHEAD_NS_NB_MAX
-#define LMHEAD_NS_NB_MAX 6
-#endif
-constexpr int NS_NB_MAX = LMHEAD_NS_NB_MAX;  // column blocks per wave
+constexpr int NR_KC = 256;          // K per chunk
+constexpr int NR_CPR = NR_KC / 8;   // 16-byte hidden pieces per row per chunk
+constexpr int NR_CB = NR_KC / 2;    // code bytes per weight row per chunk
+constexpr int NR_SB = NR_KC / 16;   // scale bytes per weight row per chunk
 
-constexpr int NS_SEGQ = 16;                 // quads per LDS segment of block scales
-constexpr int NS_SROW = NS_SEGQ + 1;        // 8-byte LDS words per weight row (1 word pad: banks)
+__device__ __forceinline__ int nr_hslot(int row, int ch) { return row * NR_CPR + (ch ^ (row & 15)); }
 
-__device__ __forceinline__ int ns_hslot(int row, int ch) { return row * NS_CPR + (ch ^ (row & 15)); }
+// LDS slot of 16-byte piece p (K-step p of the chunk) of row `row` of a code
+// unit: rows of 128 bytes, pieces xor-swizzled by row pair so the 16 rows one
+// operand read touches fall in distinct banks.
+__device__ __forceinline__ int nr_cslot(int row, int p) { return row * 8 + (p ^ ((row >> 1) & 7)); }
 
 // 4 x 4 transpose of 32-bit words across the four 16-lane rows of a wave:
 // on entry row g holds words D[g][0..3] in x0..x3; on exit x_t in row g
@@ -206,8 +183,331 @@ __device__ __forceinline__ void transpose4(uint32_t &x0, uint32_t &x1, uint32_t 
   x3 = d[1];
 }
 
+// Ring kernel, one or two row blocks (M <= 32). K is walked in chunks of 256
+// elements: per weight row 128 code bytes and 16 scale bytes. Each wave owns
+// NB column blocks of 16 rows; a block's chunk is one "unit", whose codes
+// come to LDS by two direct-to-LDS loads of 8 rows x 128 contiguous bytes
+// into a ring of NSL slots per wave. Units are read and refilled one at a
+// time, as in the bf16 weight-streaming kernel, so NSL - 1 units stay in
+// flight. A lane's ds_read_b128 takes the 16 code bytes of one K-step of its
+// row; a 4 x 4 transpose of 32-bit words across the four 16-lane groups (two
+// v_permlane32_swap, two v_permlane16_swap) hands each lane the 8 codes of
+// its MFMA slots for four K-steps. Dequantisation stays in registers:
+// v_cvt_scalef32_pk_f32_fp4 (scale 1.0) turns two codes into two fp32 values,
+// a multiply by the E4M3 block scale (v_cvt_f32_fp8) gives the exact weight,
+// whose upper 16 bits are its bf16 pattern. Hidden rows come through LDS in
+// the same 256-element chunks, double-buffered, one LDS barrier per chunk.
+//
+// Block scales are 16 bytes per row and chunk. Loaded per chunk (16 rows x
+// 16 bytes per instruction) the same 128-byte scale lines are read eight
+// times, a chunk apart, with the code stream passing through L2 in between:
+// measured without the K-steps, that stream took 78 µs instead of 37 µs
+// (M = 1, H = 2048, V = 151936). So a block's scales are loaded for a group of
+// eight chunks at once, 16 rows x 64 contiguous bytes per instruction (two
+// instructions): lane (i, k) holds row i's scales of chunk 4h + k of the
+// group, and at each chunk a ds_bpermute hands every lane of row i the
+// 16 bytes of that chunk. The next group's scales are loaded at the group's
+// last chunk, into the registers just read.
+//
+// With the K-steps the kernel is bound by the dequantisation's VALU work
+// (about 2 instructions per weight: counters show the VALU busy about half of
+// the cycles), which overlaps the stream only in part: a variant with the
+// dequantisation replaced by one instruction per K-step ran in 39 µs.
+//
+// Issue order: at the read of unit v (and in the prologue for v < 0) a
+// "batch": unit v + NSL's two direct loads; the hidden loads of chunk
+// (v + NSL) / NB when unit v + NSL starts a chunk; and, when v lies in the
+// last chunk of a scale group, the next group's two scale loads of v's
+// block. The prologue issues the batches of v = -NSL .. -1 with the first
+// group's scale loads where a steady-state batch would carry scale loads, so
+// every batch size is a function of the position only and each wait below is
+// a compile-time count of the loads issued after the ones it needs.
+constexpr int pow2_at_least(int n, int p = 1) { return p >= n ? p : pow2_at_least(n, 2 * p); }
+
+template <int NB, int NSL, int HL>
+struct NvSchedule {
+  static constexpr int GROUP = 8;  // chunks per scale group
+  static constexpr int md(int a, int m) { return ((a % m) + m) % m; }
+  static constexpr int chunk8(int v) { return md(v >= 0 ? v / NB : -((-v + NB - 1) / NB), GROUP); }
+  static constexpr int hid(int w) { return md(w, NB) == 0 ? HL : 0; }
+  static constexpr int scl(int v) { return chunk8(v) == GROUP - 1 ? 2 : 0; }
+  static constexpr int batch(int v) { return 2 + hid(v + NSL) + scl(v); }
+  // before the first read of unit u: loads after unit u's two direct loads
+  static constexpr int wait_unit(int u) {
+    int n = hid(u) + scl(u - NSL);
+    for (int v = u - NSL + 1; v <= u - 1; ++v) n += batch(v);
+    return n;
+  }
+  // before the first read of a scale group at unit u (the group's first
+  // chunk): the group was loaded last in batch u - NB
+  static constexpr int wait_scale(int u) {
+    int n = 0;
+    for (int v = u - NB + 1; v <= u - 1; ++v) n += batch(v);
+    return n;
+  }
+  static constexpr int wait_first(int u) {
+    return chunk8(u) == 0 && wait_scale(u) < wait_unit(u) ? wait_scale(u) : wait_unit(u);
+  }
+  // hidden chunks held in registers at once: chunk c is issued in batch
+  // c NB - NSL and stored at the end of unit c NB - 1 (rounded up to a power
+  // of two, which keeps the period short)
+  static constexpr int NHR = pow2_at_least((NSL - 1) / NB + 1);
+  // units per unrolled period: slots, register sets, scale groups and the two
+  // LDS hidden buffers all at compile-time positions
+  static constexpr int PERIOD = lcm_c(lcm_c(lcm_c(NB * GROUP, NSL), NB * NHR), 2 * NB);
+  // at the end of the chunk whose last unit is u (after batch u): loads
+  // after the next chunk's hidden loads, which sit in batch u + 1 - NSL
+  static constexpr int wait_hidden(int u) {
+    int n = scl(u + 1 - NSL);
+    for (int v = u + 2 - NSL; v <= u; ++v) n += batch(v);
+    return n;
+  }
+};
+
+template <int R, int NB, int NW, int NSL>
+__global__ __launch_bounds__(64 * NW, 1) void nvfp4_ring_kernel(
+    const uint16_t *__restrict__ hidden, int64_t M, int64_t H, const uint8_t *__restrict__ codes,
+    const uint8_t *__restrict__ scales, int64_t V, float scale, const float *__restrict__ bias,
+    uint16_t *__restrict__ out) {
+  constexpr int THREADS = 64 * NW;
+  constexpr int ROWS = 16 * R;
+  constexpr int HPC = ROWS * NR_CPR;                 // hidden pieces per chunk
+  constexpr int HL = (HPC + THREADS - 1) / THREADS;  // ... per thread
+  using S = NvSchedule<NB, NSL, HL>;
+  constexpr int NHR = S::NHR;
+  constexpr int PERIOD = S::PERIOD;
+  constexpr int GROUP = S::GROUP;
+  static_assert(NSL > NB && NSL <= 8, "a ring of more slots than blocks, at most 8");
+  constexpr int CW = NW * 128;  // 16-byte slots of one ring slot's codes, all waves
+  __shared__ u32x4 hs[2][HPC];
+  __shared__ u32x4 C0[CW], C1[CW], C2[NSL > 2 ? CW : 1], C3[NSL > 3 ? CW : 1],
+      C4[NSL > 4 ? CW : 1], C5[NSL > 5 ? CW : 1], C6[NSL > 6 ? CW : 1], C7[NSL > 7 ? CW : 1];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int li = lane & 15;
+  const int lg = lane >> 4;
+  const int64_t nmb = (M + 63) / 64;
+  const int64_t m0 = ((int64_t)blockIdx.x % nmb) * 64;
+  const int64_t ncb = (V + 15) / 16;
+  const int64_t tw = (int64_t)(gridDim.x / nmb) * NW;
+  const int64_t g = ((int64_t)blockIdx.x / nmb) * NW + wave;
+  const int64_t cb0 = g * ncb / tw, cb1 = (g + 1) * ncb / tw;
+  const bool active = cb1 > cb0;
+  const int64_t cend = cb1 * 16 < V ? cb1 * 16 : V;
+
+  const int64_t HC = H / 2, HS = H / 16;
+  const int64_t wrows = active ? cend - cb0 * 16 : 0;
+  const rsrc_t cr = make_rsrc(codes + (active ? cb0 * 16 : 0) * HC, (uint32_t)(wrows * HC));
+  const rsrc_t sr = make_rsrc(scales + (active ? cb0 * 16 : 0) * HS, (uint32_t)(wrows * HS));
+  const uint32_t cjs = (uint32_t)(16 * HC), sjs = (uint32_t)(16 * HS);
+  uint32_t cvoff[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int piece = (lane % 8) ^ ((4 * h + lane / 16) & 7);
+    cvoff[h] = (uint32_t)((lane / 8 + 8 * h) * HC + 16 * piece);
+  }
+
+  const int64_t nc = (H + NR_KC - 1) / NR_KC;
+  const int64_t nunits = nc * NB;
+  const bool half_tail = (H % NR_KC) != 0;
+
+  auto cslot = [&](auto jc) -> u32x4 * {
+    constexpr int J = decltype(jc)::value;
+    if constexpr (J == 0) return C0;
+    else if constexpr (J == 1) return C1;
+    else if constexpr (J == 2) return C2;
+    else if constexpr (J == 3) return C3;
+    else if constexpr (J == 4) return C4;
+    else if constexpr (J == 5) return C5;
+    else if constexpr (J == 6) return C6;
+    else return C7;
+  };
+  // Unit u (block j) into ring slot jc: two direct loads, or two loads of
+  // nothing past the last unit (the schedule's counts stay exact).
+  auto issue_unit = [&](int64_t u, auto jc, int j) {
+    const bool ok = u < nunits;
+    const int64_t c = u / NB;
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+      dma16_lds(cr, &cslot(jc)[wave * 128 + 64 * h], cvoff[h],
+                ok ? (uint32_t)(j * cjs + c * NR_CB) : OFF_NONE);
+  };
+
+  // Scales of block j, group q: load h (chunks 4h .. 4h + 3 of the group) gives
+  // lane (i, k) row i's 16 bytes of chunk 8q + 4h + k; past the last chunk,
+  // an out-of-range offset (zeros).
+  u32x4 sc[NB][2];
+  auto load_scales = [&](int j, int64_t q) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int64_t c = GROUP * q + 4 * h + lg;
+      sc[j][h] = load16(sr, c < nc ? (uint32_t)(li * HS + c * NR_SB) : OFF_NONE, (uint32_t)(j * sjs));
+    }
+  };
+
+  const int64_t hrows = M - m0 < 64 ? M - m0 : 64;
+  const rsrc_t hr = make_rsrc(hidden + m0 * H, (uint32_t)(hrows * H * 2));
+  const int64_t hpieces = H / 8;
+  uint32_t hvoff[HL];
+  int hsl[HL], hch[HL];
+#pragma unroll
+  for (int i = 0; i < HL; ++i) {
+    const int idx = i * THREADS + tid < HPC ? i * THREADS + tid : HPC - 1;
+    const int row = idx / NR_CPR, ch = idx % NR_CPR;
+    hvoff[i] = (uint32_t)((row * H + 8 * ch) * 2);
+    hsl[i] = nr_hslot(row, ch);
+    hch[i] = ch;
+  }
+  u32x4 hring[NHR][HL];
+  auto load_hidden = [&](u32x4 (&dst)[HL], int64_t c) {
+    const uint32_t soff = c < nc ? (uint32_t)(c * NR_KC * 2) : OFF_NONE;
+#pragma unroll
+    for (int i = 0; i < HL; ++i)
+      dst[i] = load16(hr, (c * NR_CPR + hch[i] < hpieces) ? hvoff[i] : OFF_NONE, soff);
+  };
+  auto store_hidden = [&](const u32x4 (&src)[HL], int buf) {
+#pragma unroll
+    for (int i = 0; i < HL; ++i) hs[buf][hsl[i]] = src[i];
+  };
+
+  f32x4 acc[NB][R];
+#pragma unroll
+  for (int j = 0; j < NB; ++j)
+#pragma unroll
+    for (int r = 0; r < R; ++r) acc[j][r] = zero4();
+
+  // A unit's codes and scale bytes in registers, copied from its slot (which
+  // is then refilled at once).
+  struct Regs {
+    uint32_t x[8];   // codes of K-step t for this lane's slot group
+    uint32_t sw[4];  // scale bytes, pre-shifted for this lane's group
+  };
+
+  // Reads unit ub + Q's slot into registers and issues its batch.
+  auto read_slot = [&](auto qc, int64_t ub, Regs &rg) {
+    constexpr int Q = decltype(qc)::value;  // position of the schedule
+    constexpr int J = Q % NB;
+    constexpr int SLOT = Q % NSL;
+    constexpr int C8 = (Q / NB) % GROUP;
+    const int64_t w = ub + Q;
+    wait_vm<S::wait_first(Q)>();
+    const u32x4 *cs = cslot(std::integral_constant<int, SLOT>{}) + wave * 128;
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const u32x4 v = cs[nr_cslot(li, 4 * q + lg)];
+      rg.x[4 * q + 0] = v[0];
+      rg.x[4 * q + 1] = v[1];
+      rg.x[4 * q + 2] = v[2];
+      rg.x[4 * q + 3] = v[3];
+    }
+    // this chunk's scale bytes of row li, from lane li + 16 (C8 % 4)
+    const int src = 4 * (li + 16 * (C8 % 4));
+#pragma unroll
+    for (int d = 0; d < 4; ++d)
+      rg.sw[d] = (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)sc[J][C8 / 4][d]) >> (8 * (lg >> 1));
+    // the batch: refill the slot once its reads have returned, the next
+    // chunk's hidden loads, the next scale group
+    wait_lds();
+    issue_unit(w + NSL, std::integral_constant<int, SLOT>{}, (Q + NSL) % NB);
+    if constexpr ((Q + NSL) % NB == 0)
+      load_hidden(hring[((Q + NSL) / NB) % NHR], (w + NSL) / NB);
+    if constexpr (C8 == GROUP - 1) load_scales(J, w / NB / GROUP + 1);
+    transpose4(rg.x[0], rg.x[1], rg.x[2], rg.x[3]);
+    transpose4(rg.x[4], rg.x[5], rg.x[6], rg.x[7]);
+  };
+
+  // Unit P of the period starting at unit ub (a multiple of PERIOD): its
+  // slot read and batch, then its K-steps.
+  auto unit = [&](auto pc, int64_t ub) {
+    constexpr int P = decltype(pc)::value;
+    constexpr int J = P % NB;
+    constexpr int BUF = (P / NB) & 1;
+    const int64_t u = ub + P;
+    const int64_t c = u / NB;
+    Regs rg;
+    read_slot(pc, ub, rg);
+    const bool half = half_tail && c == nc - 1;  // wave-uniform
+    auto kstep_t = [&](auto tc) {
+      constexpr int T = decltype(tc)::value;
+      u32x4 a[R];
+#pragma unroll
+      for (int r = 0; r < R; ++r)
+        a[r] = hs[BUF][nr_hslot(16 * r + li, 4 * T + lg)];
+      const float s = __builtin_amdgcn_cvt_f32_fp8(rg.sw[T / 2], 2 * (T % 2));
+      const u32x4 b = dequant8_fast(rg.x[T], s);
+#pragma unroll
+      for (int r = 0; r < R; ++r) acc[J][r] = kstep(acc[J][r], a[r], b);
+    };
+    static_for<4>([&](auto tc) { kstep_t(tc); });
+    if (!half) static_for<4>([&](auto tc) { kstep_t(std::integral_constant<int, 4 + decltype(tc)::value>{}); });
+    if constexpr (J == NB - 1) {
+      wait_vm<S::wait_hidden(P)>();
+      store_hidden(hring[(P / NB + 1) % NHR], BUF ^ 1);
+      lds_barrier();
+    }
+  };
+
+  // prologue: the batches of v = -NSL .. -1 (the first scale group where a
+  // steady-state batch carries scale loads), hidden chunk 0 to LDS
+  static_for<NSL>([&](auto wc) {
+    constexpr int W_ = decltype(wc)::value;
+    constexpr int VB = W_ - NSL;  // the batch this is
+    issue_unit(W_, wc, W_ % NB);
+    if constexpr (W_ % NB == 0) load_hidden(hring[(W_ / NB) % NHR], W_ / NB);
+    if constexpr (S::scl(VB) != 0) load_scales(S::md(VB, NB), 0);
+  });
+  wait_vm<S::wait_hidden(-1)>();
+  store_hidden(hring[0], 0);
+  lds_barrier();
+
+  int64_t ub = 0;
+  for (; ub + PERIOD <= nunits; ub += PERIOD) static_for<PERIOD>([&](auto pc) { unit(pc, ub); });
+  static_for<PERIOD>([&](auto pc) {
+    if (ub + decltype(pc)::value < nunits) unit(pc, ub);
+  });
+
+  if (!active) return;
+  store_blocks<R, NB>([&](int i, int j) -> f32x4 & { return acc[j][i]; }, out, m0,
+                      M - m0 < 16 * R ? M - m0 : 16 * R, cb0 * 16, cend, V, scale, bias);
+}
+
+template <int R, int NB, int NW, int NSL>
+hipError_t launch_ring_nb(const Nvfp4Args &a, int64_t nvs, hipStream_t stream) {
+  dim3 grid((unsigned)(nvs * ((a.M + 63) / 64)));
+  return launch_kernel(nvfp4_ring_kernel<R, NB, NW, NSL>, grid, dim3(64 * NW), stream,
+                       a.hidden, a.M, a.H, a.codes, a.scales, a.V, a.scale, a.bias, a.out);
+}
+
+template <int R, int NBM, int NW, int NSL>
+hipError_t launch_ring_split(const Nvfp4Args &a, const VSplit &sp, hipStream_t stream) {
+  if constexpr (NBM > 1) {
+    if (sp.nb < NBM) return launch_ring_split<R, NBM - 1, NW, NSL>(a, sp, stream);
+  }
+  return launch_ring_nb<R, NBM, NW, NSL>(a, sp.nvs, stream);
+}
+
+// ---------------------------------------------------------------------------
+// Three or four row blocks (M = 33 .. 64): the MFMA work per unit is four
+// times larger, and the ring's hidden chunks (48-64 KB) and registers do not
+// fit beside four slots per wave; this kernel streams the codes straight
+// into registers instead.
+//
+constexpr int NS_WAVES = 8;
+constexpr int NS_THREADS = 64 * NS_WAVES;
+constexpr int NS_KC = 128;          // K per quad == K per LDS chunk of hidden
+constexpr int NS_CPR = NS_KC / 8;   // 16-byte hidden pieces per row per chunk
+constexpr int NS_P = 2;             // quads of weight loads in flight ahead of use
+constexpr int NS_NB_MAX = 6;        // column blocks per wave
+
+constexpr int NS_SEGQ = 16;                 // quads per LDS segment of block scales
+constexpr int NS_SROW = NS_SEGQ + 1;        // 8-byte LDS words per weight row (1 word pad: banks)
+
+__device__ __forceinline__ int ns_hslot(int row, int ch) { return row * NS_CPR + (ch ^ (row & 15)); }
+
 template <int R, int NB>
-__global__ __launch_bounds__(NS_THREADS, 1) void nvfp4_stream_kernel(
+__global__ __launch_bounds__(NS_THREADS, 1) void nvfp4_quad_kernel(
     const uint16_t *__restrict__ hidden, int64_t M, int64_t H, const uint8_t *__restrict__ codes,
     const uint8_t *__restrict__ scales, int64_t V, float scale, const float *__restrict__ bias,
     uint16_t *__restrict__ out) {
@@ -389,24 +689,31 @@ __global__ __launch_bounds__(NS_THREADS, 1) void nvfp4_stream_kernel(
 }
 
 template <int R, int NB>
-hipError_t launch_stream_nb(const Nvfp4Args &a, int64_t nvs, hipStream_t stream) {
+hipError_t launch_quad_nb(const Nvfp4Args &a, int64_t nvs, hipStream_t stream) {
   dim3 grid((unsigned)(nvs * ((a.M + 63) / 64)));
-  return launch_kernel(nvfp4_stream_kernel<R, NB>, grid, dim3(NS_THREADS), stream, a.hidden, a.M,
+  return launch_kernel(nvfp4_quad_kernel<R, NB>, grid, dim3(NS_THREADS), stream, a.hidden, a.M,
                        a.H, a.codes, a.scales, a.V, a.scale, a.bias, a.out);
 }
 
 // The variant with NB = the split's blocks per wave (NB <= NBM).
 template <int R, int NBM>
-hipError_t launch_stream_split(const Nvfp4Args &a, const VSplit &sp, hipStream_t stream) {
+hipError_t launch_quad_split(const Nvfp4Args &a, const VSplit &sp, hipStream_t stream) {
   if constexpr (NBM > 1) {
-    if (sp.nb < NBM) return launch_stream_split<R, NBM - 1>(a, sp, stream);
+    if (sp.nb < NBM) return launch_quad_split<R, NBM - 1>(a, sp, stream);
   }
-  return launch_stream_nb<R, NBM>(a, sp.nvs, stream);
+  return launch_quad_nb<R, NBM>(a, sp.nvs, stream);
 }
 
+// One or two row blocks: the ring kernel, sixteen waves of up to three blocks
+// (16 or 32 KB of hidden chunks, 4 slots of 2 KB per wave); three or four:
+// the register-streaming kernel, eight waves of up to six blocks.
 template <int R>
 hipError_t launch_stream_r(const Nvfp4Args &a, hipStream_t stream) {
-  return launch_stream_split<R, NS_NB_MAX>(a, vsplit((a.V + 15) / 16, NS_WAVES, NS_NB_MAX), stream);
+  const int64_t ncb = (a.V + 15) / 16;
+  if constexpr (R <= 2)
+    return launch_ring_split<R, 3, 16, 4>(a, vsplit(ncb, 16, 3), stream);
+  else
+    return launch_quad_split<R, NS_NB_MAX>(a, vsplit(ncb, NS_WAVES, NS_NB_MAX), stream);
 }
 
 }  // namespace
@@ -417,9 +724,9 @@ hipError_t launch_nvfp4(const Nvfp4Args &a, hipStream_t stream) {
   if (a.M > 64) return launch_tiled_nvfp4(a, stream);
   const int64_t rows = a.M < 64 ? a.M : 64;
   const int rb = (int)((rows + 15) / 16);
-  // the streaming kernel reads 8 scale bytes at a time: rows of 8k bytes on an
-  // 8-byte aligned base
-  if (a.H % NS_KC == 0 && reinterpret_cast<uintptr_t>(a.scales) % 8 == 0) {
+  // the streaming kernels load 8 or 16 scale bytes per row at a time: rows of
+  // 8k bytes on a 16-byte aligned base
+  if (a.H % 128 == 0 && reinterpret_cast<uintptr_t>(a.scales) % 16 == 0) {
     switch (rb) {
       case 1: return launch_stream_r<1>(a, stream);
       case 2: return launch_stream_r<2>(a, stream);

@@ -1,0 +1,85 @@
+// ring.hpp -- compile-time helpers of the weight-streaming kernels
+// (internal): loops with compile-time indices and explicit waits for vector
+// memory loads.
+#pragma once
+
+#include <type_traits>
+
+#include "kstep.hpp"
+
+namespace lmhead {
+
+// Calls f(std::integral_constant<int, 0>{}) ... f(integral_constant<N - 1>)
+// in order: loops whose index must be a compile-time constant.
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F &&f) {
+  if constexpr (N > 0) {
+    static_for<N - 1>(f);
+    f(std::integral_constant<int, N - 1>{});
+  }
+}
+
+constexpr int gcd_c(int a, int b) { return b == 0 ? a : gcd_c(b, a % b); }
+constexpr int lcm_c(int a, int b) { return a / gcd_c(a, b) * b; }
+
+// Waits until at most N of this wave's vector memory loads are outstanding.
+// Loads complete in issue order, so this retires every load but the last N
+// issued. Fenced, so the compiler moves no instruction across it.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt field");
+  constexpr int ENC = (N & 15) | ((N >> 4) << 14) | 0x70 | 0xF00;  // vmcnt(N) only
+  sched_fence();
+  __builtin_amdgcn_s_waitcnt(ENC);
+  sched_fence();
+}
+
+// Waits until this wave's LDS operations have completed (lgkmcnt(0)): before
+// a direct-to-LDS load overwrites LDS this wave has just read, since such a
+// load writes LDS on its own path, not behind the wave's earlier ds_reads.
+__device__ __forceinline__ void wait_lds() {
+  sched_fence();
+  __builtin_amdgcn_s_waitcnt(0xC07F);
+}
+
+// The issue schedule of a wave that streams its weight through a ring of NSL
+// LDS slots, in units: unit u is (chunk u / NB, column block u % NB). Its LPU
+// direct loads are issued when unit u - NSL has been read (units 0 .. NSL - 1
+// in the prologue), into slot u % NSL; right after the loads of a chunk's
+// first unit come the HL hidden loads of that chunk, into register set
+// (chunk % NHR). Vector memory loads complete in issue order, so each wait is
+// "all but the loads issued after X".
+template <int NB, int NSL, int HL, int LPU>
+struct Schedule {
+  static constexpr int hid(int w) { return ((w % NB) + NB) % NB == 0 ? HL : 0; }
+  // before the first read of unit u: loads issued after unit u's
+  static constexpr int wait_unit(int u) {
+    int n = hid(u);
+    for (int w = u + 1; w <= u + NSL - 1; ++w) n += LPU + hid(w);
+    return n;
+  }
+  // at the end of the chunk whose last unit is u, after unit u + NSL was
+  // issued: loads issued after the next chunk's hidden loads (which follow
+  // unit u + 1's)
+  static constexpr int wait_hidden(int u) {
+    int n = 0;
+    for (int w = u + 2; w <= u + NSL; ++w) n += LPU + hid(w);
+    return n;
+  }
+  // hidden chunks held in registers at once: chunk c is issued with unit
+  // c NB - NSL and written to LDS at the end of chunk c - 1
+  static constexpr int NHR = (NSL - 1) / NB + 1;
+  // units per unrolled period: slots, register sets and the two LDS hidden
+  // buffers all at compile-time positions
+  static constexpr int PERIOD = lcm_c(lcm_c(NB * NHR, NSL), 2 * NB);
+};
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+// One direct-to-LDS load of 16 bytes per active lane: lane l's bytes land at
+// LDS dst + 16 l (dst wave-uniform).
+__device__ __forceinline__ void dma16_lds(rsrc_t r, void *dst, uint32_t voff, uint32_t soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t *)dst, 16, voff, soff, 0, 0);
+}
+
+}  // namespace lmhead
