@@ -393,6 +393,56 @@ def cpu_baseline(wl, h, W, budget_s=12.0):
             "ns_per_mac_1thread": None if ns_mac is None else round(ns_mac, 3)}
 
 
+def cpu_per_config(wl):
+    """The oracle timed on each workload of the pages' configurations (the
+    tiny head, the spec-decode target, the NVFP4 head at M = 256 and the
+    prefill batch), on a stated sample where the whole call would take long:
+    wall time, multiply-adds and ns per multiply-add of each timed call."""
+    import oracle
+    res = {}
+
+    def timed(fn):
+        t0 = time.perf_counter()
+        fn()
+        return time.perf_counter() - t0
+
+    w = wl.TINY
+    h, W = wl.hidden(w), wl.weight(w)
+    dt = timed(lambda: oracle.lmhead_logits(h, W, w.alphas[0], None, "f32"))
+    macs = w.M * w.H * w.V
+    res["tiny"] = {"sample": "whole call (M=4, H=256, V=4096)", "s": round(dt, 4), "macs": macs,
+                   "ns_per_mac": round(dt / macs * 1e9, 4)}
+
+    w = wl.SPEC
+    h, W, b = wl.hidden(w), wl.weight(w), wl.bias(w)
+    dt = timed(lambda: oracle.lmhead_logits(h, W, w.alphas[0], b, "f32"))
+    macs = w.M * w.H * w.V
+    res["spec_M128"] = {"sample": "whole call (M=128, H=2048, V=151936, bias)", "s": round(dt, 3),
+                        "macs": macs, "ns_per_mac": round(dt / macs * 1e9, 4)}
+    del W
+
+    w = wl.NVFP4
+    nv = 16384
+    h, c, sc = wl.hidden(w, 256), wl.codes(w, 0, nv), wl.scales(w, 0, nv)
+    dt = timed(lambda: oracle.lmhead_logits_nvfp4(h, c, sc, w.g))
+    macs = 256 * w.H * nv
+    res["nvfp4_M256"] = {"sample": f"M=256, first {nv} of {w.V} vocabulary rows, H={w.H}",
+                         "s": round(dt, 3), "macs": macs, "ns_per_mac": round(dt / macs * 1e9, 4),
+                         "s_full_vocab_est": round(dt * w.V / nv, 2)}
+
+    w = wl.PREFILL
+    rows = sorted(set(range(0, w.M, 16)) | {w.M - 1})
+    h, W = wl.hidden_rows(w, rows), wl.weight(w)
+    dt = timed(lambda: oracle.lmhead_logits(h, W, w.alphas[0], None, "f32"))
+    macs = len(rows) * w.H * w.V
+    res["prefill_M2048"] = {"sample": f"{len(rows)} of {w.M} rows (every 16th and the last), "
+                                      f"all {w.V} vocabulary rows, H={w.H}",
+                            "s": round(dt, 3), "macs": macs, "ns_per_mac": round(dt / macs * 1e9, 4),
+                            "s_all_rows_est": round(dt * w.M / len(rows), 2)}
+    del W
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -496,6 +546,8 @@ def main():
         line["vs_probes"] = ctx
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(wl, dec["h"], dec["W"])
+        del dec["W"]
+        line["cpu_baseline"]["per_config"] = cpu_per_config(wl)
     print(json.dumps(line), flush=True)
 
 

@@ -134,6 +134,10 @@ lmhead_status lmhead_logits_ex(const void *hidden, int64_t M, int64_t H, const v
  *   row_max[m]    = max over v of t[m, v]
  *   row_argmax[m] = the lowest v with t[m, v] == row_max[m]
  *   row_sumexp[m] = sum over v of exp(t[m, v] - row_max[m])   (>= 1)
+ * Logits of -inf (a masked vocabulary entry, through a -inf bias) are
+ * allowed and contribute exp(-inf) = 0; a row whose logits are all -inf gets
+ * row_max -inf, row_argmax its lowest column and row_sumexp 0. +inf and NaN
+ * logits are outside the contract.
  * so that the row's log-sum-exp is row_max + log(row_sumexp) and
  * softmax(t)[m, v] = exp(t[m, v] - row_max[m]) / row_sumexp[m]. These feed
  * the target and draft heads' acceptance distributions (vLLM PR 49120,
@@ -248,7 +252,12 @@ size_t lmhead_quantize_nvfp4_workspace_bytes(void);
 int lmhead_shape_ok(int64_t M, int64_t H, int64_t V, int nvfp4);
 
 /* Host-only: the lmhead_path the AUTO choice takes for this shape, or
- * LMHEAD_PATH_NONE when the shape is outside the contract. */
+ * LMHEAD_PATH_NONE when the shape is outside the contract. The tests use it
+ * to assert which kernel a call takes, as the sglang PR 32370 digest's test
+ * changes (test coverage of test_fp32_lm_head.py: the probe_mm interceptor
+ * asserts which torch operation, input dtype and out_dtype a call used, and a
+ * fallback case checks the explicit-fp32 path) check the path as well as the
+ * values. */
 int lmhead_path_for(int64_t M, int64_t H, int64_t V, int nvfp4);
 
 /* Static, human-readable name of a status code. */

@@ -302,6 +302,10 @@ __device__ __forceinline__ void store_rows_lds(Acc &&acc, OutT *out, float *stg,
 // [M, V] logits. The logit t is the epilogue value above, so the partials
 // reduce exactly the fp32 logits the plain call writes.
 //
+// Logits of -inf (masked entries) are allowed: a block of only -inf keeps
+// its lowest column and sums 0, and contributes nothing to a row that has a
+// finite logit. +inf and NaN logits are outside the contract.
+//
 // A block's partial depends only on the block's 16 logits and their lane
 // positions (column c0 + li in lane 16 g + li): the maximum and its column
 // are exact, and the sum is a fixed butterfly over the 16 lanes, in which
@@ -398,7 +402,10 @@ __device__ __forceinline__ void reduce_blocks(Acc &&acc, RowPart *__restrict__ p
         const float t = ok ? epilogue_v(acc(i, j)[q], alpha, has_bias, b) : -__builtin_inff();
         const float m = row16_max(t);
         const int mi = row16_min(ok && t == m ? (int)col : 0x7FFFFFFF);
-        const float e = row16_sum(ok ? exp_fast(__fsub_rn(t, m)) : 0.0f);
+        // a block whose logits are all -inf (a masked vocabulary range) has
+        // m = -inf and sums nothing: exp(t - m) would be exp(-inf + inf)
+        const bool live = ok && m != -__builtin_inff();
+        const float e = row16_sum(live ? exp_fast(__fsub_rn(t, m)) : 0.0f);
         const int r = 16 * i + 4 * lg + q;  // row within the wave's rows
         if (li == q && r < rows) part[(rbase + r) * ncb + cb] = RowPart{m, e, mi, 0};
       }

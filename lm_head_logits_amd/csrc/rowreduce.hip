@@ -36,8 +36,10 @@ struct RowAcc {
 
 // (m, i) is the larger maximum, ties to the lower column; each sum is
 // rescaled to the new maximum and the two are added. Symmetric in a and b.
-// An empty side (s == 0) contributes nothing and never reaches the
-// exponential with an infinite difference.
+// An empty side (s == 0: no column yet, or only -inf logits) contributes
+// nothing and never reaches the exponential with an infinite difference; a
+// side with s > 0 has a finite maximum, and r.m >= it, so its difference is
+// finite or the exponential of -inf (0).
 __device__ __forceinline__ RowAcc fold(RowAcc a, RowAcc b) {
   RowAcc r = a;
   max_lowest(r.m, r.i, b.m, b.i);

@@ -159,10 +159,13 @@ def sumexp_bound(x, m, V):
     Returned in binary64, per row."""
     x = np.asarray(x, dtype=np.float64)
     m = np.asarray(m, dtype=np.float64)[:, None]
-    e = np.exp(x - m)
+    d = x - m
+    e = np.exp(d)
     ncb = (V + 15) // 16
     L = 4 + (ncb + 1023) // 1024 + 6 + 4
-    return (e * 3 * U32 * np.abs(x - m)).sum(axis=1) + e.sum(axis=1) * 8 * L * U32
+    # a -inf logit (masked entry) contributes an exact 0
+    per = np.where(e > 0, e * 3 * U32 * np.abs(np.where(e > 0, d, 0.0)), 0.0)
+    return per.sum(axis=1) + e.sum(axis=1) * 8 * L * U32
 
 
 def check_rowreduce_self(gmax, garg, gsum, x):

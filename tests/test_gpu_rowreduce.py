@@ -235,3 +235,46 @@ def test_vocabulary_shards_fold_to_the_full_row():
     from helpers import sumexp_bound
     ref = np.exp(x.astype(np.float64) - x.max(axis=1, keepdims=True)).sum(axis=1)
     assert np.all(np.abs(s - ref) <= 2 * sumexp_bound(x, x.max(axis=1), V))
+
+
+@pytest.mark.parametrize("path", PATHS)
+def test_masked_blocks_minus_inf_bias(path):
+    # A -inf bias masks vocabulary entries: whole 16-column blocks, part of a
+    # block and the ragged last block. Masked entries contribute exp(-inf) = 0;
+    # the result must match the reduction of the plain call's logits and the
+    # oracle's, and be the same on both kernels.
+    rng = np.random.default_rng(77)
+    M, H, V = 37, 96, 4133
+    say(f"rowreduce -inf bias via {path}")
+    h, W = _rand_bf16(rng, (M, H), 1.0), _rand_bf16(rng, (V, H), 0.02)
+    bias = rng.normal(0, 0.1, V).astype(np.float32)
+    for lo, hi in ((16, 48), (1024, 1040), (100, 106), (4128, 4133), (2000, 2400)):
+        bias[lo:hi] = -np.inf
+    hd, Wd, bd = bf16_dev(h), bf16_dev(W), f32_dev(bias)
+    mx, am, se, lg = L.logits_rowreduce(hd, Wd, 0.25, bd, write_logits=True, path=path)
+    plain = host_f32(L.logits(hd, Wd, 0.25, bd, torch.float32))
+    assert np.array_equal(host_bits(lg), plain.view(np.uint32))
+    assert np.isneginf(plain[:, 20]).all()
+    check_rowreduce_self(_np(mx), _np(am), _np(se), plain)
+    ref_m, _, _, ref_x, A = oracle.lmhead_rowreduce(h, W, 0.25, bias)
+    A = np.where(np.isfinite(ref_x), A, 0.0)
+    check_rowreduce_oracle(_np(mx), _np(am), _np(se), ref_m, ref_x, A, V)
+    other = "tiled" if path == "skinny" else "skinny"
+    mx2, am2, se2, _ = L.logits_rowreduce(hd, Wd, 0.25, bd, path=other)
+    for a, b in ((mx, mx2), (am, am2), (se, se2)):
+        assert np.array_equal(_np(a).view(np.uint32), _np(b).view(np.uint32))
+
+
+@pytest.mark.parametrize("path", PATHS)
+def test_fully_masked_rows(path):
+    # Every logit -inf: the row maximum is -inf, its lowest column 0, and the
+    # sum 0 (the contract for rows with no finite logit).
+    rng = np.random.default_rng(78)
+    M, H, V = 5, 64, 300
+    say(f"rowreduce all -inf via {path}")
+    hd = bf16_dev(_rand_bf16(rng, (M, H), 1.0))
+    Wd = bf16_dev(_rand_bf16(rng, (V, H), 0.02))
+    bd = f32_dev(np.full(V, -np.inf, np.float32))
+    mx, am, se, _ = L.logits_rowreduce(hd, Wd, 1.0, bd, path=path)
+    assert np.isneginf(_np(mx)).all()
+    assert np.all(_np(am) == 0) and np.all(_np(se) == 0.0)
