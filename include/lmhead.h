@@ -7,7 +7,14 @@
  * (W4A16) variant with bf16 output. Every output row depends only on its own
  * hidden row, the weight, alpha, bias and the output type: never on how many
  * rows are in the call, where the row sits in it, or which entry point (bf16
- * weight at any M) produced it.
+ * weight at any M) produced it. Each logit is summed over K in one fixed
+ * order, starting at a point that depends on H and on the column's index v
+ * within the call (in groups of 10240 columns) and wrapping around; so a call
+ * on a row sub-range W + v0*H of the vocabulary (one GPU's shard) gives the
+ * full call's columns bit for bit when v0 is a multiple of
+ * 10240 * (H / 256) / gcd(5, H / 256) (any v0 when H % 256 != 0 or
+ * H == 256: every column then starts at 0), and agrees with them within the
+ * fp32 accumulation tolerance otherwise.
  *
  * Where the operation is defined (page title, then section):
  *  - bf16 x bf16 products accumulated at fp32 with fp32 logits and no fp32

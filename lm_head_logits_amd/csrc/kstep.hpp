@@ -8,14 +8,16 @@
 // element with exactly this chain and nothing else:
 //
 //   acc = +0.0f
-//   for k0 = 0, 32, 64, ..., H - 32 (ascending):
+//   for k0 = s, s + 32, ..., H - 32, 0, 32, ..., s - 32   (s = korder_start(v, H)):
 //       acc = MFMA_F32_16x16x32_BF16(acc, h[m, k0 .. k0+31], w[v, k0 .. k0+31])
 //
 // with one fixed placement of the 32 products inside the instruction (the
-// operand map below). There is no split-K, no second accumulator and no
-// cross-lane reduction of partial sums, so the bits of (m, v) depend only on
-// hidden row m and weight row v: not on M, on the 16-row block or row slot the
-// row lands in, or on which kernel ran.
+// operand map below). The start s depends on the column v and H only
+// (korder.hpp: it staggers the weight stream over HBM). There is no split-K,
+// no second accumulator and no cross-lane reduction of partial sums, so the
+// bits of (m, v) depend only on hidden row m, weight row v and the index v:
+// not on M, on the 16-row block or row slot the row lands in, or on which
+// kernel ran.
 //
 // Operand map of one K-step (16 x 16 output block at rows r0.., cols c0..):
 //   lane l = 16*g + i  (i = l % 16, g = l / 16)

@@ -109,7 +109,11 @@ __global__ __launch_bounds__(256) void nvfp4_generic_kernel(const uint16_t *__re
 
   const u32x4 z = {0u, 0u, 0u, 0u};
   const int64_t nk = H / KSTEP;
-  for (int64_t s = 0; s < nk; ++s) {
+  // the wave's 64 columns lie in one group of korder.hpp: their chains start
+  // at K-step krot of the row
+  const int64_t krot = korder_start(col0, H) / KSTEP;
+  for (int64_t s0 = 0; s0 < nk; ++s0) {
+    const int64_t s = s0 + krot < nk ? s0 + krot : s0 + krot - nk;  // K-step of the row
     u32x4 b[NV_NB], a[R];
 #pragma unroll
     for (int j = 0; j < NV_NB; ++j) {
@@ -268,7 +272,7 @@ template <int R, int NB, int NW, int NSL>
 __global__ __launch_bounds__(64 * NW, 1) void nvfp4_ring_kernel(
     const uint16_t *__restrict__ hidden, int64_t M, int64_t H, const uint8_t *__restrict__ codes,
     const uint8_t *__restrict__ scales, int64_t V, float scale, const float *__restrict__ bias,
-    uint16_t *__restrict__ out) {
+    uint16_t *__restrict__ out, int64_t gblocks, int64_t kwg) {
   constexpr int THREADS = 64 * NW;
   constexpr int ROWS = 16 * R;
   constexpr int HPC = ROWS * NR_CPR;                 // hidden pieces per chunk
@@ -291,9 +295,9 @@ __global__ __launch_bounds__(64 * NW, 1) void nvfp4_ring_kernel(
   const int64_t nmb = (M + 63) / 64;
   const int64_t m0 = ((int64_t)blockIdx.x % nmb) * 64;
   const int64_t ncb = (V + 15) / 16;
-  const int64_t tw = (int64_t)(gridDim.x / nmb) * NW;
-  const int64_t g = ((int64_t)blockIdx.x / nmb) * NW + wave;
-  const int64_t cb0 = g * ncb / tw, cb1 = (g + 1) * ncb / tw;
+  const WaveCols wc = split_cols((int64_t)blockIdx.x / nmb, (int64_t)gridDim.x / nmb, wave, NW, ncb,
+                                 gblocks, kwg, H);
+  const int64_t cb0 = wc.cb0, cb1 = wc.cb1;
   const bool active = cb1 > cb0;
   const int64_t cend = cb1 * 16 < V ? cb1 * 16 : V;
 
@@ -312,6 +316,10 @@ __global__ __launch_bounds__(64 * NW, 1) void nvfp4_ring_kernel(
   const int64_t nc = (H + NR_KC - 1) / NR_KC;
   const int64_t nunits = nc * NB;
   const bool half_tail = (H % NR_KC) != 0;
+  // chunk c of the order -> chunk of the row (a start other than 0 only when
+  // H % 256 == 0: then no chunk is half)
+  const int64_t krot = wc.kstart / NR_KC;
+  auto rowchunk = [&](int64_t c) { return c + krot < nc ? c + krot : c + krot - nc; };
 
   auto cslot = [&](auto jc) -> u32x4 * {
     constexpr int J = decltype(jc)::value;
@@ -328,11 +336,11 @@ __global__ __launch_bounds__(64 * NW, 1) void nvfp4_ring_kernel(
   // nothing past the last unit (the schedule's counts stay exact).
   auto issue_unit = [&](int64_t u, auto jc, int j) {
     const bool ok = u < nunits;
-    const int64_t c = u / NB;
+    const int64_t pc = ok ? rowchunk(u / NB) : 0;
 #pragma unroll
     for (int h = 0; h < 2; ++h)
       dma16_lds(cr, &cslot(jc)[wave * 128 + 64 * h], cvoff[h],
-                ok ? (uint32_t)(j * cjs + c * NR_CB) : OFF_NONE);
+                ok ? (uint32_t)(j * cjs + pc * NR_CB) : OFF_NONE);
   };
 
   // Scales of block j, group q: load h (chunks 4h .. 4h + 3 of the group) gives
@@ -343,7 +351,8 @@ __global__ __launch_bounds__(64 * NW, 1) void nvfp4_ring_kernel(
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const int64_t c = GROUP * q + 4 * h + lg;
-      sc[j][h] = load16(sr, c < nc ? (uint32_t)(li * HS + c * NR_SB) : OFF_NONE, (uint32_t)(j * sjs));
+      sc[j][h] = load16(sr, c < nc ? (uint32_t)(li * HS + rowchunk(c) * NR_SB) : OFF_NONE,
+                        (uint32_t)(j * sjs));
     }
   };
 
@@ -362,10 +371,11 @@ __global__ __launch_bounds__(64 * NW, 1) void nvfp4_ring_kernel(
   }
   u32x4 hring[NHR][HL];
   auto load_hidden = [&](u32x4 (&dst)[HL], int64_t c) {
-    const uint32_t soff = c < nc ? (uint32_t)(c * NR_KC * 2) : OFF_NONE;
+    const int64_t pc = c < nc ? rowchunk(c) : c;
+    const uint32_t soff = c < nc ? (uint32_t)(pc * NR_KC * 2) : OFF_NONE;
 #pragma unroll
     for (int i = 0; i < HL; ++i)
-      dst[i] = load16(hr, (c * NR_CPR + hch[i] < hpieces) ? hvoff[i] : OFF_NONE, soff);
+      dst[i] = load16(hr, (pc * NR_CPR + hch[i] < hpieces) ? hvoff[i] : OFF_NONE, soff);
   };
   auto store_hidden = [&](const u32x4 (&src)[HL], int buf) {
 #pragma unroll
@@ -474,10 +484,11 @@ __global__ __launch_bounds__(64 * NW, 1) void nvfp4_ring_kernel(
 }
 
 template <int R, int NB, int NW, int NSL>
-hipError_t launch_ring_nb(const Nvfp4Args &a, int64_t nvs, hipStream_t stream) {
-  dim3 grid((unsigned)(nvs * ((a.M + 63) / 64)));
+hipError_t launch_ring_nb(const Nvfp4Args &a, const VSplit &sp, hipStream_t stream) {
+  dim3 grid((unsigned)(sp.nvs * ((a.M + 63) / 64)));
   return launch_kernel(nvfp4_ring_kernel<R, NB, NW, NSL>, grid, dim3(64 * NW), stream,
-                       a.hidden, a.M, a.H, a.codes, a.scales, a.V, a.scale, a.bias, a.out);
+                       a.hidden, a.M, a.H, a.codes, a.scales, a.V, a.scale, a.bias, a.out,
+                       sp.gblocks, sp.kwg);
 }
 
 template <int R, int NBM, int NW, int NSL>
@@ -485,7 +496,7 @@ hipError_t launch_ring_split(const Nvfp4Args &a, const VSplit &sp, hipStream_t s
   if constexpr (NBM > 1) {
     if (sp.nb < NBM) return launch_ring_split<R, NBM - 1, NW, NSL>(a, sp, stream);
   }
-  return launch_ring_nb<R, NBM, NW, NSL>(a, sp.nvs, stream);
+  return launch_ring_nb<R, NBM, NW, NSL>(a, sp, stream);
 }
 
 // ---------------------------------------------------------------------------
@@ -510,7 +521,7 @@ template <int R, int NB>
 __global__ __launch_bounds__(NS_THREADS, 1) void nvfp4_quad_kernel(
     const uint16_t *__restrict__ hidden, int64_t M, int64_t H, const uint8_t *__restrict__ codes,
     const uint8_t *__restrict__ scales, int64_t V, float scale, const float *__restrict__ bias,
-    uint16_t *__restrict__ out) {
+    uint16_t *__restrict__ out, int64_t gblocks, int64_t kwg) {
   constexpr int ROWS = 16 * R;
   constexpr int HPC = ROWS * NS_CPR;
   constexpr int HL = (HPC + NS_THREADS - 1) / NS_THREADS;
@@ -531,12 +542,15 @@ __global__ __launch_bounds__(NS_THREADS, 1) void nvfp4_quad_kernel(
   const int lg = lane >> 4;
   const int64_t nmb = (M + 63) / 64;
   const int64_t m0 = ((int64_t)blockIdx.x % nmb) * 64;
-  // Column blocks [cb0, cb1) of this wave: the ncb blocks split evenly over
-  // the grid's waves along V (at most NB each), as in the bf16 kernel.
+  // Column blocks [cb0, cb1) of this wave: the ncb blocks split over the
+  // grid's waves along V group by group (at most NB each), as in the bf16
+  // kernel; [wg_cb0, wg_cb1) those of the work-group.
   const int64_t ncb = (V + 15) / 16;
-  const int64_t tw = (int64_t)(gridDim.x / nmb) * NS_WAVES;
-  const int64_t g0 = ((int64_t)blockIdx.x / nmb) * NS_WAVES;  // the work-group's first wave
-  const int64_t cb0 = (g0 + wave) * ncb / tw, cb1 = (g0 + wave + 1) * ncb / tw;
+  const int64_t wg = (int64_t)blockIdx.x / nmb, nwg = (int64_t)gridDim.x / nmb;
+  const WaveCols wc = split_cols(wg, nwg, wave, NS_WAVES, ncb, gblocks, kwg, H);
+  const int64_t cb0 = wc.cb0, cb1 = wc.cb1;
+  const int64_t wg_cb0 = split_cols(wg, nwg, 0, NS_WAVES, ncb, gblocks, kwg, H).cb0;
+  const int64_t wg_cb1 = split_cols(wg, nwg, NS_WAVES, NS_WAVES, ncb, gblocks, kwg, H).cb0;
   const bool active = cb1 > cb0;
   const int64_t cend = cb1 * 16 < V ? cb1 * 16 : V;
 
@@ -552,11 +566,13 @@ __global__ __launch_bounds__(NS_THREADS, 1) void nvfp4_quad_kernel(
   // in memory; each segment of NS_SEGQ quads (8 scale bytes per row per quad)
   // is loaded cooperatively into LDS, so the scale stream is read once, in
   // order.
-  const int64_t wg_cb0 = g0 * ncb / tw, wg_cb1 = (g0 + NS_WAVES) * ncb / tw;
   const int64_t wg_row0 = wg_cb0 * 16;
   const int64_t wg_rows = (wg_cb1 * 16 < V ? wg_cb1 * 16 : V) - wg_row0;
   const rsrc_t sr = make_rsrc(scales + wg_row0 * HS, (uint32_t)(wg_rows * HS));
   const int64_t nq = H / NS_KC;
+  // quad q of the order -> quad of the row
+  const int64_t krot = wc.kstart / NS_KC;
+  auto rowquad = [&](int64_t q) { return q + krot < nq ? q + krot : q + krot - nq; };
   // Scale piece i of this thread in segment `seg`: its load offset (pieces past
   // the segment or the tile get an out-of-range offset and read zero) and its
   // LDS word.
@@ -565,7 +581,7 @@ __global__ __launch_bounds__(NS_THREADS, 1) void nvfp4_quad_kernel(
     const int p = i * NS_THREADS + tid;
     const int row = p / NS_SEGQ, e = p % NS_SEGQ;
     return (i < SL && p < SPIECES && e < seg_quads)
-               ? (uint32_t)(row * HS + (seg * NS_SEGQ + e) * 8) : 0x80000000u;
+               ? (uint32_t)(row * HS + rowquad(seg * NS_SEGQ + e) * 8) : 0x80000000u;
   };
   auto scale_store = [&](int i, u32x2 v) {
     const int p = i * NS_THREADS + tid;
@@ -601,7 +617,7 @@ __global__ __launch_bounds__(NS_THREADS, 1) void nvfp4_quad_kernel(
   u32x4 hreg[HL];
   auto load_hidden = [&](int64_t q) {
 #pragma unroll
-    for (int i = 0; i < HL; ++i) hreg[i] = load16(hr, hvoff[i], (uint32_t)(q * NS_KC * 2));
+    for (int i = 0; i < HL; ++i) hreg[i] = load16(hr, hvoff[i], (uint32_t)(rowquad(q) * NS_KC * 2));
   };
   auto store_hidden = [&](int buf) {
 #pragma unroll
@@ -611,7 +627,7 @@ __global__ __launch_bounds__(NS_THREADS, 1) void nvfp4_quad_kernel(
   u32x4 cq[P][NB];
   auto load_q = [&](int slot, int64_t q) {
 #pragma unroll
-    for (int j = 0; j < NB; ++j) cq[slot][j] = load16(cr, cvoff, (uint32_t)(q * 64 + j * cjs));
+    for (int j = 0; j < NB; ++j) cq[slot][j] = load16(cr, cvoff, (uint32_t)(rowquad(q) * 64 + j * cjs));
   };
 
   f32x4 acc[NB][R];
@@ -689,10 +705,10 @@ __global__ __launch_bounds__(NS_THREADS, 1) void nvfp4_quad_kernel(
 }
 
 template <int R, int NB>
-hipError_t launch_quad_nb(const Nvfp4Args &a, int64_t nvs, hipStream_t stream) {
-  dim3 grid((unsigned)(nvs * ((a.M + 63) / 64)));
+hipError_t launch_quad_nb(const Nvfp4Args &a, const VSplit &sp, hipStream_t stream) {
+  dim3 grid((unsigned)(sp.nvs * ((a.M + 63) / 64)));
   return launch_kernel(nvfp4_quad_kernel<R, NB>, grid, dim3(NS_THREADS), stream, a.hidden, a.M,
-                       a.H, a.codes, a.scales, a.V, a.scale, a.bias, a.out);
+                       a.H, a.codes, a.scales, a.V, a.scale, a.bias, a.out, sp.gblocks, sp.kwg);
 }
 
 // The variant with NB = the split's blocks per wave (NB <= NBM).
@@ -701,7 +717,7 @@ hipError_t launch_quad_split(const Nvfp4Args &a, const VSplit &sp, hipStream_t s
   if constexpr (NBM > 1) {
     if (sp.nb < NBM) return launch_quad_split<R, NBM - 1>(a, sp, stream);
   }
-  return launch_quad_nb<R, NBM>(a, sp.nvs, stream);
+  return launch_quad_nb<R, NBM>(a, sp, stream);
 }
 
 // One or two row blocks: the ring kernel, sixteen waves of up to three blocks
@@ -711,9 +727,9 @@ template <int R>
 hipError_t launch_stream_r(const Nvfp4Args &a, hipStream_t stream) {
   const int64_t ncb = (a.V + 15) / 16;
   if constexpr (R <= 2)
-    return launch_ring_split<R, 3, 16, 4>(a, vsplit(ncb, 16, 3), stream);
+    return launch_ring_split<R, 3, 16, 4>(a, vsplit(ncb, a.H, 16, 3), stream);
   else
-    return launch_quad_split<R, NS_NB_MAX>(a, vsplit(ncb, NS_WAVES, NS_NB_MAX), stream);
+    return launch_quad_split<R, NS_NB_MAX>(a, vsplit(ncb, a.H, NS_WAVES, NS_NB_MAX), stream);
 }
 
 }  // namespace

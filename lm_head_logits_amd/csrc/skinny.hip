@@ -24,8 +24,17 @@
 // instruction (16 rows, the MFMA operand layout read straight into
 // registers), which capped the H = 2048 head at about 4.4 TB/s.
 //
-// Launch: one work-group per CU, the vocabulary's column blocks split evenly
-// over all waves (each owns floor or ceil of the mean, NB = the ceiling).
+// The waves' lockstep also means that the ~4000 weight rows read at any one
+// time are read at one offset within their rows, which on some allocations
+// uses only part of HBM's channels (the same decode head measured at 5.9 or
+// at 4.3-4.6 TB/s). The K orders of korder.hpp start 10240-column groups at
+// different offsets, so the grid's reads spread over eight or sixteen
+// offsets.
+//
+// Launch: one work-group per CU, the vocabulary's column blocks split group
+// by group over the work-groups (about in proportion to the group's blocks:
+// a work-group's columns share one K order) and evenly over a group's waves
+// (each owns floor or ceil of the mean, NB = the largest).
 // The stream's bandwidth follows the number of CUs streaming, and a CU that
 // holds two work-groups while others hold one finishes last (at V = 151936:
 // 297 work-groups of 32 blocks took 1.4x as long as 238 of 40). With few
@@ -69,7 +78,7 @@ template <int R, int NB, bool F16, typename OutT, int NW, int NSL>
 __global__ __launch_bounds__(64 * NW, NW >= 8 ? 1 : 2) void skinny_kernel(
     const uint16_t *__restrict__ hidden, int64_t M, int64_t H, const uint16_t *__restrict__ W,
     int64_t V, float alpha, const float *__restrict__ bias, OutT *__restrict__ out,
-    RowPart *__restrict__ part) {
+    RowPart *__restrict__ part, int64_t gblocks, int64_t kwg) {
   constexpr int THREADS = 64 * NW;
   constexpr int ROWS = 16 * R;
   constexpr int HPC = ROWS * SK_CPR;                 // hidden pieces per chunk
@@ -93,12 +102,14 @@ __global__ __launch_bounds__(64 * NW, NW >= 8 ? 1 : 2) void skinny_kernel(
   const int lg = lane >> 4;
   const int64_t nmb = (M + 63) / 64;
   const int64_t m0 = ((int64_t)blockIdx.x % nmb) * 64;
-  // This wave's column blocks [cb0, cb1): the ncb blocks split evenly over
-  // all waves of the grid along V, at most NB each (the host sized NB so).
+  // This wave's column blocks [cb0, cb1): the ncb blocks split over the
+  // grid's waves along V, group by group (korder.hpp), at most NB each (the
+  // host sized NB so); kstart: the K element where the chains of the
+  // work-group's columns start.
   const int64_t ncb = (V + 15) / 16;
-  const int64_t tw = (int64_t)(gridDim.x / nmb) * NW;
-  const int64_t g = ((int64_t)blockIdx.x / nmb) * NW + wave;
-  const int64_t cb0 = g * ncb / tw, cb1 = (g + 1) * ncb / tw;
+  const WaveCols wc = split_cols((int64_t)blockIdx.x / nmb, (int64_t)gridDim.x / nmb, wave, NW, ncb,
+                                 gblocks, kwg, H);
+  const int64_t cb0 = wc.cb0, cb1 = wc.cb1;
   const bool active = cb1 > cb0;  // wave-uniform
   const int64_t cend = cb1 * 16 < V ? cb1 * 16 : V;  // end of this wave's columns
 
@@ -139,15 +150,20 @@ __global__ __launch_bounds__(64 * NW, NW >= 8 ? 1 : 2) void skinny_kernel(
   const int64_t nchunks = (nk + 1) / 2;  // the last may hold one K-step (H % 64 == 32)
   const int64_t nunits = nchunks * NB;
   const bool odd_tail = (nk & 1) != 0;
+  // chunk c of the order -> chunk of the row (a start other than 0 only when
+  // H % 256 == 0, so then there is no half chunk)
+  const int64_t krot = wc.kstart / SK_KC;
+  auto rowchunk = [&](int64_t c) { return c + krot < nchunks ? c + krot : c + krot - nchunks; };
 
   u32x4 hring[NHR][HL];
   auto load_hidden = [&](u32x4 (&dst)[HL], int64_t c) {
-    const uint32_t soff = c < nchunks ? (uint32_t)(c * SK_KC * 2) : OFF_NONE;
+    const int64_t pc = c < nchunks ? rowchunk(c) : c;
+    const uint32_t soff = c < nchunks ? (uint32_t)(pc * SK_KC * 2) : OFF_NONE;
 #pragma unroll
     for (int i = 0; i < HL; ++i) {
       // a piece past the row end (H % 64 == 32) reads zero through an
       // out-of-range offset
-      const uint32_t v = (c * SK_CPR + hch[i] < hpieces) ? hvoff[i] : OFF_NONE;
+      const uint32_t v = (pc * SK_CPR + hch[i] < hpieces) ? hvoff[i] : OFF_NONE;
       dst[i] = load16(hr, v, soff);
     }
   };
@@ -173,8 +189,7 @@ __global__ __launch_bounds__(64 * NW, NW >= 8 ? 1 : 2) void skinny_kernel(
   // slot unused) past the last unit, which keep the load counts of the
   // schedule exact.
   auto issue_unit = [&](int64_t u, u32x4 *wl, int j) {
-    const int64_t c = u / NB;
-    const uint32_t soff = u < nunits ? (uint32_t)(c * 128 + j * wjstride) : OFF_NONE;
+    const uint32_t soff = u < nunits ? (uint32_t)(rowchunk(u / NB) * 128 + j * wjstride) : OFF_NONE;
 #pragma unroll
     for (int h = 0; h < 2; ++h)
       dma16_lds(wr, &wl[wave * SK_WSLOT + 64 * h], lvoff[h],
@@ -253,11 +268,11 @@ __global__ __launch_bounds__(64 * NW, NW >= 8 ? 1 : 2) void skinny_kernel(
 }
 
 template <int R, int NB, bool F16, typename OutT, int NW, int NSL>
-hipError_t launch_nb(const GemmArgs &a, int64_t nvs, hipStream_t stream) {
-  dim3 grid((unsigned)(nvs * ((a.M + 63) / 64)));
+hipError_t launch_nb(const GemmArgs &a, const VSplit &sp, hipStream_t stream) {
+  dim3 grid((unsigned)(sp.nvs * ((a.M + 63) / 64)));
   return launch_kernel(skinny_kernel<R, NB, F16, OutT, NW, NSL>, grid, dim3(64 * NW), stream,
                        a.hidden, a.M, a.H, a.W, a.V, a.alpha, a.bias, static_cast<OutT *>(a.out),
-                       static_cast<RowPart *>(a.part));
+                       static_cast<RowPart *>(a.part), sp.gblocks, sp.kwg);
 }
 
 // The variant with NB = the split's blocks per wave (NB <= NBM), sixteen
@@ -267,7 +282,7 @@ hipError_t launch_split(const GemmArgs &a, const VSplit &sp, hipStream_t stream)
   if constexpr (NBM > 1) {
     if (sp.nb < NBM) return launch_split<R, NBM - 1, F16, OutT>(a, sp, stream);
   }
-  return launch_nb<R, NBM, F16, OutT, 16, 4>(a, sp.nvs, stream);
+  return launch_nb<R, NBM, F16, OutT, 16, 4>(a, sp, stream);
 }
 
 template <int R, bool F16, typename OutT>
@@ -275,10 +290,10 @@ hipError_t launch_r(const GemmArgs &a, hipStream_t stream) {
   const int64_t ncb = (a.V + 15) / 16, cus = device_cus();
   // few column blocks per CU: one block per wave, fewer waves, a deeper ring
   // (at most 128 KB of stage slots per work-group)
-  if (ncb <= 4 * cus) return launch_nb<R, 1, F16, OutT, 4, 8>(a, vsplit(ncb, 4, 1).nvs, stream);
-  if (ncb <= 8 * cus) return launch_nb<R, 1, F16, OutT, 8, 8>(a, vsplit(ncb, 8, 1).nvs, stream);
+  if (ncb <= 4 * cus) return launch_nb<R, 1, F16, OutT, 4, 8>(a, vsplit(ncb, a.H, 4, 1), stream);
+  if (ncb <= 8 * cus) return launch_nb<R, 1, F16, OutT, 8, 8>(a, vsplit(ncb, a.H, 8, 1), stream);
   constexpr int NBM = sk_nb_max<R>();
-  return launch_split<R, NBM, F16, OutT>(a, vsplit(ncb, 16, NBM), stream);
+  return launch_split<R, NBM, F16, OutT>(a, vsplit(ncb, a.H, 16, NBM), stream);
 }
 
 template <bool F16, typename OutT>

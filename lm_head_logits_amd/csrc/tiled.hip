@@ -149,6 +149,19 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void tiled_kernel(TiledArgs args) 
   }
   const uint32_t row8 = (uint32_t)(8 * H * 2);  // bytes of 8 rows
 
+  // H % 32 == 0 but not necessarily % 64: the last stage may hold one K-step
+  // (its second half is loaded but never read).
+  const int64_t nsteps = H / KSTEP;  // >= 1
+  const int64_t nstages = (nsteps + 1) / 2;
+  // Stage kt of the tile's K order -> stage of the row: the chains of the
+  // tile's columns start korder_start(n0, H) elements into the row (a start
+  // other than 0 only when H % 256 == 0, so then every stage is whole).
+  // Stages past the last stay past it.
+  const int64_t krot = korder_start(n0, H) / TL_TK;
+  auto rowstage = [&](int64_t kt) {
+    return kt >= nstages ? kt : (kt + krot < nstages ? kt + krot : kt + krot - nstages);
+  };
+
   // NVFP4 producer: unit u = tid + i * threads is half `u % 2` (32 elements)
   // of stage row u / 2; its codes and scales for one stage sit in registers.
   constexpr int NT = 64 * NW;
@@ -157,14 +170,15 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void tiled_kernel(TiledArgs args) 
   u32x4 cq[NU > 0 ? NU : 1];
   uint32_t sq[NU > 0 ? NU : 1];
   auto load_codes = [&](int64_t kt) {
+    const int64_t pk = rowstage(kt);
 #pragma unroll
     for (int i = 0; i < NU; ++i) {
       const int u = tid + i * NT, row = u >> 1, half = u & 1;
       // a half past the row's end (H % 64 == 32, or the stage after the
       // last) reads zero through an out-of-range offset
-      const bool in = kt * TL_TK + 32 * half < H;
-      const uint32_t co = in ? (uint32_t)(row * (H / 2) + kt * 32 + 16 * half) : OFF_NONE;
-      const uint32_t so = in ? (uint32_t)(row * (H / 16) + kt * 4 + 2 * half) : OFF_NONE;
+      const bool in = pk * TL_TK + 32 * half < H;
+      const uint32_t co = in ? (uint32_t)(row * (H / 2) + pk * 32 + 16 * half) : OFF_NONE;
+      const uint32_t so = in ? (uint32_t)(row * (H / 16) + pk * 4 + 2 * half) : OFF_NONE;
       cq[i] = load16(br, co, 0);
       sq[i] = __builtin_amdgcn_raw_buffer_load_b16(sr, so, 0, 0);
     }
@@ -186,7 +200,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void tiled_kernel(TiledArgs args) 
   // decoded from the codes loaded one stage earlier, whose registers are then
   // refilled with stage kt+1's.
   auto issue_stage = [&](int64_t kt, u32x4 *as, u32x4 *bs) {
-    const uint32_t soff = (uint32_t)(kt * TL_TK * 2);
+    const uint32_t soff = (uint32_t)(rowstage(kt) * TL_TK * 2);
     if constexpr (NV) decode_codes(bs);
 #pragma unroll
     for (int u = 0; u < A_DMA; ++u) {
@@ -210,10 +224,6 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void tiled_kernel(TiledArgs args) 
 #pragma unroll
     for (int j = 0; j < FN; ++j) acc[i][j] = zero4();
 
-  // H % 32 == 0 but not necessarily % 64: the last stage may hold one K-step
-  // (its second half is loaded but never read).
-  const int64_t nsteps = H / KSTEP;  // >= 1
-  const int64_t nstages = (nsteps + 1) / 2;
 
   auto compute = [&](const u32x4 *as, const u32x4 *bs, int s) {
     u32x4 a[FM], bb[FN];

@@ -4,6 +4,8 @@ sample that includes the ragged vocabulary tail), integer-valued inputs are
 checked bit for bit at every full shape, and the row-invariance contract is
 checked bit for bit across row counts, row orders, target/draft calls and
 vocabulary sub-ranges."""
+import math
+
 import numpy as np
 import pytest
 import torch
@@ -135,16 +137,20 @@ def test_spec_rows_invariant_to_order_and_draft_gather(spec):
 
 
 def test_spec_vocab_shard_equals_full(spec):
+    # Column v's K order starts at ((v // 10240) * 5 mod (H / 256)) * 256, v
+    # counted within the call: a vocabulary shard reproduces the full call's
+    # columns bit for bit when its first column is a multiple of
+    # 10240 * (H / 256) (5 and H / 256 = 8 coprime here), at any width,
+    # ragged end included.
     w, h, W, b, hd, Wd, bd = spec
     alpha = w.alphas[0]
     full = L.logits(hd, Wd, alpha, bd)
-    V8 = w.V // 8
-    for r in (0, 3, 7):
-        v0 = r * V8
-        part = L.logits(hd, Wd[v0:v0 + V8], alpha, bd[v0:v0 + V8])
-        assert torch.equal(ibits(part), ibits(full[:, v0:v0 + V8])), r
-        part32 = L.logits(hd[:32].contiguous(), Wd[v0:v0 + V8], alpha, bd[v0:v0 + V8])
-        assert torch.equal(ibits(part32), ibits(full[:32, v0:v0 + V8])), r
+    period = 10240 * (w.H // 256) // math.gcd(5, w.H // 256)
+    for v0, v1 in ((0, 18992), (0, 10240 + 16), (period, period + 18992), (period, w.V)):
+        part = L.logits(hd, Wd[v0:v1], alpha, bd[v0:v1])
+        assert torch.equal(ibits(part), ibits(full[:, v0:v1])), (v0, v1)
+        part32 = L.logits(hd[:32].contiguous(), Wd[v0:v1], alpha, bd[v0:v1])
+        assert torch.equal(ibits(part32), ibits(full[:32, v0:v1])), (v0, v1)
 
 
 @pytest.fixture(scope="module")
