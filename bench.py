@@ -21,6 +21,7 @@ from __future__ import annotations
 
 import argparse
 import hashlib
+import itertools
 import json
 import os
 import re
@@ -90,32 +91,47 @@ def committed_traffic(kernel: str):
 # GPU timing
 # ----------------------------------------------------------------------------
 
-def timed_calls(torch, fns, warmup, steps):
-    """Run `fns` (one step = each fn once) warmup + steps times. Returns the
-    step wall time (ms, events around all steps) and per-fn average launch
-    time in ms (events around each call)."""
+def timed_calls(torch, fns, warmup, steps, batches=5):
+    """Run `fns` (one step = each fn once) warmup + steps times. Each fn's
+    `steps` calls run back to back in `batches` batches, one pair of events
+    around each batch and none between calls, so a batch's time is that of
+    its kernels (an event recorded between two kernels holds the second back
+    by several microseconds). Returns the step time (ms: events around all
+    steps, divided by steps), the wall time per step (ms) and, per fn, the
+    batches' average launch times (ms)."""
     for _ in range(warmup):
         for f in fns:
             f()
     torch.cuda.synchronize()
+    nb = max(1, min(batches, steps))
+    sizes = [steps // nb + (1 if b < steps % nb else 0) for b in range(nb)]
     ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in fns] for _ in range(steps)]
+           for _ in range(nb)] for _ in fns]
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
     t0.record()
-    for s in range(steps):
-        for i, f in enumerate(fns):
-            ev[s][i][0].record()
-            f()
-            ev[s][i][1].record()
+    for i, f in enumerate(fns):
+        for b, n in enumerate(sizes):
+            ev[i][b][0].record()
+            for _ in range(n):
+                f()
+            ev[i][b][1].record()
     t1.record()
     torch.cuda.synchronize()
     wall = (time.perf_counter() - wall0) * 1e3
     total = t0.elapsed_time(t1)
-    per = [[ev[s][i][0].elapsed_time(ev[s][i][1]) for s in range(steps)] for i in range(len(fns))]
+    per = [[ev[i][b][0].elapsed_time(ev[i][b][1]) / n for b, n in enumerate(sizes)]
+           for i in range(len(fns))]
     return total / steps, wall / steps, per
+
+
+def rotating(fns):
+    """One callable that calls `fns` in turn (copies of a head that fits the
+    256 MB MALL: each call then reads its copy from HBM)."""
+    it = itertools.cycle(fns)
+    return lambda: next(it)()
 
 
 def to_dev_bf16(torch, a, dev):
@@ -158,7 +174,7 @@ def bench_shard(torch, L, w, hd, Wd, warmup, steps, shards=8, copies=4):
         out = torch.empty((M, vs), dtype=torch.float32, device=hd.device)
         fns = [(lambda i=i: L.logits(hd[:M], Wd[i * vs:(i + 1) * vs], w.alphas[1], None,
                                      torch.float32, out=out)) for i in range(copies)]
-        _, _, per = timed_calls(torch, fns, warmup, steps)
+        _, _, per = timed_calls(torch, [rotating(fns)], warmup * copies, steps * copies)
         us = 1e3 * float(np.mean(per))
         b = bytes_bf16(M, w.H, vs, 4, False)
         res[str(M)] = {"us_avg": round(us, 2), "GBps": round(b / us / 1e3, 1),
@@ -236,7 +252,7 @@ def bench_nvfp4(torch, L, wl, dev, warmup, steps, copies=4):
         out = torch.empty((M, w.V), dtype=torch.bfloat16, device=dev)
         fns = [(lambda i=i: L.logits_nvfp4(hd[:M], cs[i], ss[i], w.g, 1.0, out=out))
                for i in range(copies)]
-        _, _, per = timed_calls(torch, fns, warmup, steps)
+        _, _, per = timed_calls(torch, [rotating(fns)], warmup * copies, steps * copies)
         us = 1e3 * float(np.mean(per))
         by = bytes_nvfp4(M, w.H, w.V)
         f = flops(M, w.H, w.V)
