@@ -61,7 +61,8 @@ def flops(M, H, V):
 
 # Sources the decode kernel's code and launch depend on: a counter reading is
 # valid only while these are unchanged.
-DECODE_SOURCES = ("kstep.hpp", "launch.hpp", "lmhead_api.cpp", "skinny.hip")
+DECODE_SOURCES = ("kstep.hpp", "korder.hpp", "launch.hpp", "lmhead_api.cpp", "ring.hpp",
+                  "skinny.hip")
 
 
 def kernel_source_hash(files=DECODE_SOURCES):
@@ -349,6 +350,33 @@ def bench_copy(torch, dev, warmup, steps, nbytes=1 << 30):
             "GBps": round(2 * nbytes / us / 1e3, 1)}
 
 
+def bench_libgemm(torch, dev, warmup, steps, M=2048, H=4096, V=151936):
+    """Context, not part of the path: the vendor GEMM (hipBLASLt through
+    torch.mm) at the prefill shape, with fp32 output (out_dtype, the call the
+    sglang digest's fp32 head makes) and with bf16 output. Inputs are device
+    normals of the prefill workload's scales (the GEMM's speed does not
+    depend on the exact values)."""
+    g = torch.Generator(device=dev)
+    g.manual_seed(3)
+    a = torch.randn(M, H, generator=g, device=dev).to(torch.bfloat16)
+    w = (0.02 * torch.randn(V, H, generator=g, device=dev)).to(torch.bfloat16)
+    wt = w.t()
+    f = flops(M, H, V)
+    res = {"M": M, "H": H, "V": V}
+    legs = {"bf16_out": lambda: torch.mm(a, wt)}
+    try:
+        torch.mm(a[:16], wt, out_dtype=torch.float32)
+        legs["f32_out"] = lambda: torch.mm(a, wt, out_dtype=torch.float32)
+    except (TypeError, RuntimeError):
+        pass
+    for name, fn in legs.items():
+        _, _, per = timed_calls(torch, [fn], warmup, steps)
+        us = 1e3 * float(np.mean(per[0]))
+        res[name] = {"us_avg": round(us, 1), "TFLOPs": round(f / us / 1e6, 1),
+                     "frac_mfma": round(f / us / 1e6 / BF16_PEAK_TFLOPS, 4)}
+    return res
+
+
 # ----------------------------------------------------------------------------
 # CPU baseline: the oracle on a bounded sample of the decode workload.
 # ----------------------------------------------------------------------------
@@ -465,7 +493,7 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--only", choices=["decode", "prefill", "spec", "nvfp4", "f16", "rowreduce",
-                                       "quantize", "copy", "probes", "all"],
+                                       "quantize", "copy", "probes", "libgemm", "all"],
                     default="all",
                     help="run one workload only (for profiling; 'copy' is the HBM counter "
                          "calibration); the headline line needs decode")
@@ -493,7 +521,8 @@ def main():
               "rowreduce": lambda: bench_rowreduce(torch, L, wl, dev, args.warmup, args.steps),
               "quantize": lambda: bench_quantize(torch, L, wl, dev, args.warmup, args.steps),
               "copy": lambda: bench_copy(torch, dev, args.warmup, args.steps),
-              "probes": lambda: bench_probes(torch, L, dev, args.warmup, args.steps)}[args.only]
+              "probes": lambda: bench_probes(torch, L, dev, args.warmup, args.steps),
+              "libgemm": lambda: bench_libgemm(torch, dev, args.warmup, max(5, args.steps // 5))}[args.only]
         print(json.dumps({"workload": args.only, "result": fn()}), flush=True)
         return
     dec = bench_decode(torch, L, wl, dev, args.warmup, args.steps)
@@ -522,6 +551,11 @@ def main():
         torch.cuda.empty_cache()
     if run("probes"):
         extra["probes"] = bench_probes(torch, L, dev, args.warmup, args.steps)
+        torch.cuda.empty_cache()
+    if run("libgemm"):
+        extra["library_gemm_prefill_context"] = bench_libgemm(torch, dev, args.warmup,
+                                                              max(5, args.steps // 5))
+        torch.cuda.empty_cache()
 
     w = dec["w"]
     step_ms = dec["step_ms"]

@@ -169,11 +169,18 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void tiled_kernel(TiledArgs args) 
   static_assert(!NV || NU * NT == TN * 2, "NVFP4 producer tiling");
   u32x4 cq[NU > 0 ? NU : 1];
   uint32_t sq[NU > 0 ? NU : 1];
+  // Unit u's stage row and half. Rows 2k and 2k + 1 share their swizzle, so
+  // with the two halves of a row on neighbouring lanes, lanes writing rows
+  // 2k and 2k + 1 hit the same banks. Instead each group of 8 units takes
+  // the even or odd rows of 8 (0, 2, 4, 6 or 1, 3, 5, 7), both halves: the
+  // eight 16-byte pieces one decode store of the group writes then sit in
+  // eight distinct slots.
+  auto unit_row = [](int u) { return (u >> 4) * 8 + ((u >> 1) & 3) * 2 + ((u >> 3) & 1); };
   auto load_codes = [&](int64_t kt) {
     const int64_t pk = rowstage(kt);
 #pragma unroll
     for (int i = 0; i < NU; ++i) {
-      const int u = tid + i * NT, row = u >> 1, half = u & 1;
+      const int u = tid + i * NT, row = unit_row(u), half = u & 1;
       // a half past the row's end (H % 64 == 32, or the stage after the
       // last) reads zero through an out-of-range offset
       const bool in = pk * TL_TK + 32 * half < H;
@@ -186,7 +193,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void tiled_kernel(TiledArgs args) 
   auto decode_codes = [&](u32x4 *bs) {
 #pragma unroll
     for (int i = 0; i < NU; ++i) {
-      const int u = tid + i * NT, row = u >> 1, half = u & 1;
+      const int u = tid + i * NT, row = unit_row(u), half = u & 1;
       // elements 0-15 of the half take scale byte 0, elements 16-31 byte 1
       const float s0 = __builtin_amdgcn_cvt_f32_fp8((int)sq[i], 0);
       const float s1 = __builtin_amdgcn_cvt_f32_fp8((int)sq[i], 1);
