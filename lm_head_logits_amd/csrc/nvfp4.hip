@@ -224,50 +224,9 @@ __device__ __forceinline__ void transpose4(uint32_t &x0, uint32_t &x1, uint32_t 
 // last chunk of a scale group, the next group's two scale loads of v's
 // block. The prologue issues the batches of v = -NSL .. -1 with the first
 // group's scale loads where a steady-state batch would carry scale loads, so
-// every batch size is a function of the position only and each wait below is
-// a compile-time count of the loads issued after the ones it needs.
-constexpr int pow2_at_least(int n, int p = 1) { return p >= n ? p : pow2_at_least(n, 2 * p); }
-
-template <int NB, int NSL, int HL>
-struct NvSchedule {
-  static constexpr int GROUP = 8;  // chunks per scale group
-  static constexpr int md(int a, int m) { return ((a % m) + m) % m; }
-  static constexpr int chunk8(int v) { return md(v >= 0 ? v / NB : -((-v + NB - 1) / NB), GROUP); }
-  static constexpr int hid(int w) { return md(w, NB) == 0 ? HL : 0; }
-  static constexpr int scl(int v) { return chunk8(v) == GROUP - 1 ? 2 : 0; }
-  static constexpr int batch(int v) { return 2 + hid(v + NSL) + scl(v); }
-  // before the first read of unit u: loads after unit u's two direct loads
-  static constexpr int wait_unit(int u) {
-    int n = hid(u) + scl(u - NSL);
-    for (int v = u - NSL + 1; v <= u - 1; ++v) n += batch(v);
-    return n;
-  }
-  // before the first read of a scale group at unit u (the group's first
-  // chunk): the group was loaded last in batch u - NB
-  static constexpr int wait_scale(int u) {
-    int n = 0;
-    for (int v = u - NB + 1; v <= u - 1; ++v) n += batch(v);
-    return n;
-  }
-  static constexpr int wait_first(int u) {
-    return chunk8(u) == 0 && wait_scale(u) < wait_unit(u) ? wait_scale(u) : wait_unit(u);
-  }
-  // hidden chunks held in registers at once: chunk c is issued in batch
-  // c NB - NSL and stored at the end of unit c NB - 1 (rounded up to a power
-  // of two, which keeps the period short)
-  static constexpr int NHR = pow2_at_least((NSL - 1) / NB + 1);
-  // units per unrolled period: slots, register sets, scale groups and the two
-  // LDS hidden buffers all at compile-time positions
-  static constexpr int PERIOD = lcm_c(lcm_c(lcm_c(NB * GROUP, NSL), NB * NHR), 2 * NB);
-  // at the end of the chunk whose last unit is u (after batch u): loads
-  // after the next chunk's hidden loads, which sit in batch u + 1 - NSL
-  static constexpr int wait_hidden(int u) {
-    int n = scl(u + 1 - NSL);
-    for (int v = u + 2 - NSL; v <= u; ++v) n += batch(v);
-    return n;
-  }
-};
-
+// every batch size is a function of the position only and each wait is a
+// compile-time count of the loads issued after the ones it needs
+// (NvSchedule, ring.hpp).
 template <int R, int NB, int NW, int NSL>
 __global__ __launch_bounds__(64 * NW, 1) void nvfp4_ring_kernel(
     const uint16_t *__restrict__ hidden, int64_t M, int64_t H, const uint8_t *__restrict__ codes,

@@ -74,6 +74,52 @@ struct Schedule {
   static constexpr int PERIOD = lcm_c(lcm_c(NB * NHR, NSL), 2 * NB);
 };
 
+// The NVFP4 ring kernel's issue schedule (nvfp4.hip): units of 256-element
+// chunks with two direct loads each, the hidden loads of a chunk after its
+// first unit's, and each block's scales loaded for a group of eight chunks
+// at once.
+constexpr int pow2_at_least(int n, int p = 1) { return p >= n ? p : pow2_at_least(n, 2 * p); }
+
+template <int NB, int NSL, int HL>
+struct NvSchedule {
+  static constexpr int GROUP = 8;  // chunks per scale group
+  static constexpr int md(int a, int m) { return ((a % m) + m) % m; }
+  static constexpr int chunk8(int v) { return md(v >= 0 ? v / NB : -((-v + NB - 1) / NB), GROUP); }
+  static constexpr int hid(int w) { return md(w, NB) == 0 ? HL : 0; }
+  static constexpr int scl(int v) { return chunk8(v) == GROUP - 1 ? 2 : 0; }
+  static constexpr int batch(int v) { return 2 + hid(v + NSL) + scl(v); }
+  // before the first read of unit u: loads after unit u's two direct loads
+  static constexpr int wait_unit(int u) {
+    int n = hid(u) + scl(u - NSL);
+    for (int v = u - NSL + 1; v <= u - 1; ++v) n += batch(v);
+    return n;
+  }
+  // before the first read of a scale group at unit u (the group's first
+  // chunk): the group was loaded last in batch u - NB
+  static constexpr int wait_scale(int u) {
+    int n = 0;
+    for (int v = u - NB + 1; v <= u - 1; ++v) n += batch(v);
+    return n;
+  }
+  static constexpr int wait_first(int u) {
+    return chunk8(u) == 0 && wait_scale(u) < wait_unit(u) ? wait_scale(u) : wait_unit(u);
+  }
+  // hidden chunks held in registers at once: chunk c is issued in batch
+  // c NB - NSL and stored at the end of unit c NB - 1 (rounded up to a power
+  // of two, which keeps the period short)
+  static constexpr int NHR = pow2_at_least((NSL - 1) / NB + 1);
+  // units per unrolled period: slots, register sets, scale groups and the two
+  // LDS hidden buffers all at compile-time positions
+  static constexpr int PERIOD = lcm_c(lcm_c(lcm_c(NB * GROUP, NSL), NB * NHR), 2 * NB);
+  // at the end of the chunk whose last unit is u (after batch u): loads
+  // after the next chunk's hidden loads, which sit in batch u + 1 - NSL
+  static constexpr int wait_hidden(int u) {
+    int n = scl(u + 1 - NSL);
+    for (int v = u + 2 - NSL; v <= u; ++v) n += batch(v);
+    return n;
+  }
+};
+
 typedef __attribute__((address_space(3))) void lds_void_t;
 
 // One direct-to-LDS load of 16 bytes per active lane: lane l's bytes land at

@@ -73,3 +73,45 @@ def barriers_with_pending_lds_loads(lines, labels):
                 break
             p += 1
     return sorted(bad)
+
+
+_LGKM0 = re.compile(r"lgkmcnt\(0\)")
+
+
+def lds_loads_with_pending_lds_ops(lines, labels):
+    """Indices of direct-to-LDS loads reached on some path while an LDS
+    instruction of the same wave (a `ds_` read, write or permute) may still
+    be outstanding.
+
+    A direct-to-LDS load writes LDS on its own path, not behind the wave's
+    earlier LDS instructions, so a ring kernel that refills a slot it has
+    just read must first wait for those reads (`s_waitcnt lgkmcnt(0)`).
+    State along a path: whether a `ds_` instruction was issued since the
+    last lgkmcnt(0); followed through every branch, as above."""
+    bad = set()
+    best = {}
+    work = [(0, 0)]
+    while work:
+        p, st = work.pop()
+        while p < len(lines):
+            if best.get(p, -1) >= st:
+                break
+            best[p] = st
+            t = lines[p]
+            op = t.split()[0]
+            if op.startswith("ds_"):
+                st = 1
+            if op == "s_waitcnt" and _LGKM0.search(t):
+                st = 0
+            if op.startswith("buffer_load") and t.endswith(" lds") and st:
+                bad.add(p)
+            if op == "s_branch" or op.startswith("s_cbranch"):
+                tgt = t.split()[1]
+                if tgt in labels:
+                    work.append((labels[tgt], st))
+                if op == "s_branch":
+                    break
+            if op == "s_endpgm":
+                break
+            p += 1
+    return sorted(bad)
