@@ -261,6 +261,15 @@ def bench_nvfp4(torch, L, wl, dev, warmup, steps, copies=4):
         res[str(M)] = {"us_avg": round(us, 2), "GBps": round(by / us / 1e3, 1),
                        "TFLOPs": round(f / us / 1e6, 1), "roofline_us": round(roof, 2),
                        "frac_roofline": round(roof / us, 4)}
+    del cs, ss
+    # Side by side: the bf16 entry point on a bf16 head of the same shape
+    # (the same logits type), at the row count the tiled kernel serves.
+    Wb = (0.02 * torch.randn(w.V, w.H, device=dev)).to(torch.bfloat16)
+    for M in [m for m in w.Ms if m > 64]:
+        out = torch.empty((M, w.V), dtype=torch.bfloat16, device=dev)
+        _, _, per = timed_calls(torch, [lambda: L.logits(hd[:M], Wb, 1.0, None, torch.bfloat16,
+                                                         out=out)], warmup, steps)
+        res[str(M)]["bf16_head_same_shape_us"] = round(1e3 * float(np.mean(per[0])), 2)
     return res
 
 

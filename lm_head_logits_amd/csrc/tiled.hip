@@ -376,9 +376,12 @@ hipError_t launch_tiled(const GemmArgs &a, hipStream_t stream) {
 hipError_t launch_tiled_nvfp4(const Nvfp4Args &a, hipStream_t stream) {
   const TiledArgs t{a.hidden, a.M, a.H, nullptr, a.codes, a.scales, a.V, a.scale, a.bias, a.out,
                     nullptr};
-  // 128 x 128 tiles of four waves: measured 12% faster at M = 256 than
-  // 256 x 256 or 128 x 256 tiles (more tiles in flight per CU; the decode of
-  // each weight tile is repeated once per 128 rows of M).
+  // More than 128 rows: 256 x 256 tiles of eight waves, which decode each
+  // weight element once per 256 rows (M = 256: 190 against 213 µs for
+  // 128 x 128 tiles, measured once the decode stores were free of bank
+  // conflicts; before, the larger tile was 12% slower). Up to 128 rows:
+  // 128 x 128 tiles of four waves, two resident per CU.
+  if (a.M > 128) return launch_tm<256, 256, 4, 2, true, false, uint16_t>(t, stream);
   return launch_tm<128, 128, 2, 2, true, false, uint16_t>(t, stream);
 }
 
