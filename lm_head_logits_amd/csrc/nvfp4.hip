@@ -586,6 +586,8 @@ __global__ __launch_bounds__(NS_THREADS, 1) void nvfp4_quad_kernel(
   u32x4 cq[P][NB];
   auto load_q = [&](int slot, int64_t q) {
 #pragma unroll
+    // default policy: a quad reads 64 bytes of each 128-byte line of codes,
+    // the next quad the other half, from the cache
     for (int j = 0; j < NB; ++j) cq[slot][j] = load16(cr, cvoff, (uint32_t)(rowquad(q) * 64 + j * cjs));
   };
 

@@ -16,7 +16,8 @@ constexpr int PR_STEP = PR_THREADS * 16;     // bytes per step
 // Streams `bytes` (a multiple of 16) once: work-group w reads its own
 // contiguous segment [w * seg, (w + 1) * seg), 4 KB per step across its 256
 // lanes, PR_U steps in flight, xor-folded (the pattern that reached the
-// highest read rate among those measured on this part). The fold is stored
+// highest read rate among those measured on this part), with the read-once
+// (non-temporal) hint the weight streams of the projection carry. The fold is stored
 // only when `flag` is set (the caller passes 0), which keeps the loads live.
 __global__ __launch_bounds__(PR_THREADS) void hbm_read_kernel(const uint8_t *__restrict__ buf,
                                                               uint64_t bytes, uint64_t seg,
@@ -31,7 +32,8 @@ __global__ __launch_bounds__(PR_THREADS) void hbm_read_kernel(const uint8_t *__r
   for (uint64_t o = 0; o < seg; o += (uint64_t)PR_STEP * PR_U) {
     u32x4 v[PR_U];
 #pragma unroll
-    for (int u = 0; u < PR_U; ++u) v[u] = load16(r, lane, (uint32_t)(o + (uint64_t)u * PR_STEP));
+    for (int u = 0; u < PR_U; ++u)
+      v[u] = load16<LOAD_STREAM>(r, lane, (uint32_t)(o + (uint64_t)u * PR_STEP));
 #pragma unroll
     for (int u = 0; u < PR_U; ++u) x ^= v[u][0] ^ v[u][1] ^ v[u][2] ^ v[u][3];
   }

@@ -51,9 +51,10 @@ __device__ __forceinline__ int tl_slot(int row, int piece) {
 typedef __attribute__((address_space(3))) void lds_void;
 
 // One direct-to-LDS load: 64 lanes x 16 bytes into 1 KB of LDS at `dst`
-// (wave-uniform), lane l landing at dst + 16 l.
+// (wave-uniform), lane l landing at dst + 16 l; POLICY: the cache hint.
+template <int POLICY = LOAD_DEFAULT>
 __device__ __forceinline__ void dma16(rsrc_t r, void *dst, uint32_t voff, uint32_t soff) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)dst, 16, voff, soff, 0, 0);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)dst, 16, voff, soff, 0, POLICY);
 }
 
 // Arguments of one tiled launch. The B operand is either a 16-bit weight W
@@ -127,6 +128,15 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void tiled_kernel(TiledArgs args) 
   const int64_t t = xcd < r ? xcd * (q + 1) + pos : r * (q + 1) + (xcd - r) * q + pos;
   const int64_t m0 = (t % nmt) * TM;
   const int64_t n0 = (t / nmt) * TN;
+  // The 128-row tiles serve calls of at most 128 rows (one tile of rows):
+  // there the 16-bit weight is read once per call, in whole 128-byte lines,
+  // and its direct loads carry the read-once (non-temporal) hint, as in the
+  // weight-streaming kernels (M = 128, H = 2048: 125 against 130 µs). The
+  // 256-row tiles keep the default: prefill's row tiles share each weight
+  // tile through L2, and at M = 256 the hint measured 5% slower. A compile-
+  // time choice: a run-time one put a branch in the stage loop, and the
+  // prefill kernel ran 8% slower for it.
+  constexpr bool B_STREAM = !NV && TM == 128;
 
   const int64_t arows = M - m0 < TM ? M - m0 : TM;
   const int64_t brows = V - n0 < TN ? V - n0 : TN;
@@ -186,6 +196,9 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void tiled_kernel(TiledArgs args) 
       const bool in = pk * TL_TK + 32 * half < H;
       const uint32_t co = in ? (uint32_t)(row * (H / 2) + pk * 32 + 16 * half) : OFF_NONE;
       const uint32_t so = in ? (uint32_t)(row * (H / 16) + pk * 4 + 2 * half) : OFF_NONE;
+      // default policy: a stage reads 32 bytes of each 128-byte line of
+      // codes, and the next stages read the rest of the line from the cache
+      // (non-temporal loads here took the M = 256 call from 187 to 280 µs)
       cq[i] = load16(br, co, 0);
       sq[i] = __builtin_amdgcn_raw_buffer_load_b16(sr, so, 0, 0);
     }
@@ -220,7 +233,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void tiled_kernel(TiledArgs args) 
 #pragma unroll
       for (int u = 0; u < B_DMA; ++u) {
         const int g = wave * B_DMA + u;
-        dma16(br, &bs[g * 64], lvoff[g & 1], soff + g * row8);
+        dma16<B_STREAM ? LOAD_STREAM : LOAD_DEFAULT>(br, &bs[g * 64], lvoff[g & 1], soff + g * row8);
       }
     }
   };
