@@ -1,5 +1,6 @@
 /*
- * lmhead_probes.h -- measurement probes built into the same library.
+ * lmhead_probes.h -- measurement probes, in a library of their own
+ * (liblmhead_probes.so) beside the projection's (liblmhead.so).
  *
  * Not part of the projection: two plain kernels whose rates give the HBM read
  * bandwidth and the bf16 MFMA throughput this part sustains in practice, so

@@ -276,7 +276,7 @@ _lib.load()
 # ---------------------------------------------------------------------------
 
 def _probe_sink(device, dtype):
-    n = int(_lib.load().lmhead_probe_grid()) * 256
+    n = int(_lib.load_probes().lmhead_probe_grid()) * 256
     return torch.empty(n, dtype=dtype, device=device)
 
 
@@ -286,7 +286,7 @@ def probe_hbm_read(buf: torch.Tensor, *, stream=None) -> int:
     _need(buf.is_cuda and buf.is_contiguous(), "buf must be a contiguous CUDA tensor")
     nbytes = buf.numel() * buf.element_size()
     sink = _probe_sink(buf.device, torch.int32)
-    st = _lib.load().lmhead_probe_hbm_read(buf.data_ptr(), nbytes, 0, sink.data_ptr(),
+    st = _lib.load_probes().lmhead_probe_hbm_read(buf.data_ptr(), nbytes, 0, sink.data_ptr(),
                                            _stream_handle(buf.device, stream))
     _check(st, "lmhead_probe_hbm_read")
     return nbytes
@@ -297,7 +297,7 @@ def probe_mfma_bf16(iters: int, device="cuda", *, stream=None) -> float:
     dev = torch.device(device)
     sink = _probe_sink(dev, torch.float32)
     flops = ctypes.c_double(0.0)
-    st = _lib.load().lmhead_probe_mfma_bf16(int(iters), 0, sink.data_ptr(),
+    st = _lib.load_probes().lmhead_probe_mfma_bf16(int(iters), 0, sink.data_ptr(),
                                             _stream_handle(dev, stream), ctypes.byref(flops))
     _check(st, "lmhead_probe_mfma_bf16")
     return flops.value

@@ -1,4 +1,6 @@
-"""Compile the HIP library in-tree: lm_head_logits_amd/liblmhead.so (gfx950)."""
+"""Compile the HIP libraries in-tree (gfx950): lm_head_logits_amd/liblmhead.so,
+the projection, and lm_head_logits_amd/liblmhead_probes.so, the measurement
+probes the benchmark reports alongside it (not part of the projection)."""
 from __future__ import annotations
 
 import os
@@ -11,6 +13,8 @@ from pathlib import Path
 PKG = Path(__file__).resolve().parent
 CSRC = PKG / "csrc"
 LIB = PKG / "liblmhead.so"
+PROBES_SRC = PKG / "probes"
+PROBES_LIB = PKG / "liblmhead_probes.so"
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [
@@ -32,6 +36,10 @@ def sources():
     return sorted(CSRC.glob("*.hip")) + sorted(CSRC.glob("*.cpp"))
 
 
+def probe_sources():
+    return sorted(PROBES_SRC.glob("*.hip"))
+
+
 def _run(cmd):
     r = subprocess.run(cmd, capture_output=True, text=True)
     # the host pass does not know the packed-fp32 feature name; that warning is expected
@@ -41,10 +49,11 @@ def _run(cmd):
 
 def build(verbose: bool = False) -> Path:
     """Always recompiles (a stale library must never be picked up). Each source
-    is compiled to its own object in parallel, then the objects are linked."""
-    tmp = LIB.with_suffix(".so.tmp")
+    is compiled to its own object in parallel, then each library's objects
+    are linked. Returns the projection's library."""
     inc = ["-I", str(PKG.parent / "include")]
-    srcs = sources()
+    srcs = sources() + probe_sources()
+    libs = ((LIB, [s.name for s in sources()]), (PROBES_LIB, [s.name for s in probe_sources()]))
     with tempfile.TemporaryDirectory(prefix="lmhead_build_") as d:
         objs = [str(Path(d) / (s.name + ".o")) for s in srcs]
         cmds = [[hipcc(), *HIPCC_FLAGS, *inc, "-c", str(s), "-o", o] for s, o in zip(srcs, objs)]
@@ -58,13 +67,16 @@ def build(verbose: bool = False) -> Path:
             msgs += m
             if rc != 0:
                 raise RuntimeError(f"hipcc failed on {cmd[-3]}:\n" + "\n".join(m))
-        rc, m = _run([hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", str(tmp), *objs])
-        msgs += m
-        if rc != 0:
-            raise RuntimeError("link failed:\n" + "\n".join(m))
+        for lib, names in libs:
+            tmp = lib.with_suffix(".so.tmp")
+            mine = [str(Path(d) / (n + ".o")) for n in names]
+            rc, m = _run([hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", str(tmp), *mine])
+            msgs += m
+            if rc != 0:
+                raise RuntimeError(f"link of {lib.name} failed:\n" + "\n".join(m))
+            os.replace(tmp, lib)
     if verbose and msgs:
         print("\n".join(msgs))
-    os.replace(tmp, LIB)
     return LIB
 
 

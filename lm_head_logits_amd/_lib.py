@@ -32,14 +32,20 @@ EXPORTS = ("lmhead_logits", "lmhead_logits_path", "lmhead_logits_ex", "lmhead_lo
            "lmhead_rowreduce_workspace_bytes", "lmhead_logits_rowreduce_noalloc", "lmhead_logits_nvfp4", "lmhead_quantize_nvfp4",
            "lmhead_quantize_nvfp4_workspace_bytes", "lmhead_shape_ok",
            "lmhead_path_for", "lmhead_status_string", "lmhead_version")
-# include/lmhead_probes.h: measurement probes (not part of the projection)
+# include/lmhead_probes.h: measurement probes (not part of the projection),
+# in a library of their own
 PROBE_EXPORTS = ("lmhead_probe_grid", "lmhead_probe_hbm_read", "lmhead_probe_mfma_bf16")
 
 _lib = None
+_probes = None
 
 
 def lib_path() -> Path:
     return _build.LIB
+
+
+def probes_path() -> Path:
+    return _build.PROBES_LIB
 
 
 def load() -> ctypes.CDLL:
@@ -79,11 +85,25 @@ def load() -> ctypes.CDLL:
     lib.lmhead_status_string.argtypes = [i32]
     lib.lmhead_version.restype = ctypes.c_char_p
     lib.lmhead_version.argtypes = []
+    _lib = lib
+    return lib
+
+
+def load_probes() -> ctypes.CDLL:
+    """Load liblmhead_probes.so, the measurement probes (built with the
+    projection's library when neither exists)."""
+    global _probes
+    if _probes is not None:
+        return _probes
+    if not _build.PROBES_LIB.exists():
+        _build.build()
+    lib = ctypes.CDLL(str(_build.PROBES_LIB))
+    vp, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
     lib.lmhead_probe_grid.restype = i64
     lib.lmhead_probe_grid.argtypes = []
     lib.lmhead_probe_hbm_read.restype = i32
     lib.lmhead_probe_hbm_read.argtypes = [vp, ctypes.c_size_t, i32, vp, vp]
     lib.lmhead_probe_mfma_bf16.restype = i32
     lib.lmhead_probe_mfma_bf16.argtypes = [i64, i32, vp, vp, ctypes.POINTER(ctypes.c_double)]
-    _lib = lib
+    _probes = lib
     return lib

@@ -1,13 +1,25 @@
 // probes.hip -- measurement probes: the HBM read rate and the bf16 MFMA rate
 // this part sustains, as context for the projection's fractions of the
-// published peaks. Not part of the projection.
-#include "kstep.hpp"
-#include "launch.hpp"
+// published peaks. Not part of the projection: built into a library of its
+// own (liblmhead_probes.so), which only the benchmark and its tests load.
+#include "../csrc/kstep.hpp"
+#include "../csrc/launch.hpp"
 #include "lmhead_probes.h"
 
 namespace lmhead {
 
 namespace {
+
+// Compute units of the current device (256 on MI355X if the query fails:
+// only the probes' grid size depends on it).
+int probe_cus() {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      cus <= 0)
+    return 256;
+  return cus;
+}
 
 constexpr int PR_THREADS = 256;
 constexpr int PR_U = 8;                      // 4 KB steps in flight per work-group
@@ -80,7 +92,7 @@ __global__ __launch_bounds__(PR_THREADS) void mfma_kernel(int64_t iters, int fla
 
 extern "C" {
 
-int64_t lmhead_probe_grid(void) { return 4 * (int64_t)lmhead::device_cus(); }
+int64_t lmhead_probe_grid(void) { return 4 * (int64_t)lmhead::probe_cus(); }
 
 lmhead_status lmhead_probe_hbm_read(const void *buf, size_t bytes, int flag, uint32_t *sink,
                                     void *stream) {
@@ -103,7 +115,7 @@ lmhead_status lmhead_probe_mfma_bf16(int64_t iters, int flag, float *sink, void 
                                      double *flops) {
   if (iters <= 0 || sink == nullptr) return LMHEAD_ERR_INVALID;
   // two work-groups of four waves per CU: two waves per SIMD
-  const int64_t grid = 2 * (int64_t)lmhead::device_cus();
+  const int64_t grid = 2 * (int64_t)lmhead::probe_cus();
   if (flops != nullptr) *flops = (double)grid * 4 * (double)iters * 16 * 16384.0;
   const hipError_t e = lmhead::launch_kernel(lmhead::mfma_kernel, dim3((unsigned)grid),
                                              dim3(lmhead::PR_THREADS),

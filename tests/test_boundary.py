@@ -30,12 +30,18 @@ def test_every_header_is_checked():
 
 def test_library_exports_every_declared_symbol():
     lib = ctypes.CDLL(str(_lib.lib_path()))
-    for name in declared_functions() + declared_functions(PROBE_HEADER):
+    for name in declared_functions():
         assert hasattr(lib, name), name
+    # the measurement probes live in a library of their own
+    for name in declared_functions(PROBE_HEADER):
+        assert not hasattr(lib, name), name
+    probes = ctypes.CDLL(str(_lib.probes_path()))
+    for name in declared_functions(PROBE_HEADER):
+        assert hasattr(probes, name), name
 
 
 def test_probes_reject_bad_arguments_on_the_host():
-    lib = _lib.load()
+    lib = _lib.load_probes()
     sink = ctypes.c_void_p(16)  # never dereferenced: every call below fails its host checks
     assert lib.lmhead_probe_hbm_read(None, 1024, 0, sink, None) == _lib.ERR_INVALID
     assert lib.lmhead_probe_hbm_read(ctypes.c_void_p(256), 1000, 0, sink, None) == _lib.ERR_INVALID

@@ -16,7 +16,7 @@ DEV = "cuda:0"
 
 
 def _sink(dtype):
-    return torch.zeros(int(_lib.load().lmhead_probe_grid()) * 256, dtype=dtype, device=DEV)
+    return torch.zeros(int(_lib.load_probes().lmhead_probe_grid()) * 256, dtype=dtype, device=DEV)
 
 
 @pytest.mark.parametrize("nbytes", [16, 4096, (16 << 20) + 48, 3 * (1 << 20) + 16])
@@ -26,7 +26,7 @@ def test_hbm_probe_reads_every_piece_once(nbytes):
     words = rng.integers(0, 1 << 32, nbytes // 4, dtype=np.uint64).astype(np.uint32)
     buf = torch.from_numpy(words.view(np.int32)).to(DEV)
     sink = _sink(torch.int32)
-    st = _lib.load().lmhead_probe_hbm_read(buf.data_ptr(), nbytes, 1, sink.data_ptr(),
+    st = _lib.load_probes().lmhead_probe_hbm_read(buf.data_ptr(), nbytes, 1, sink.data_ptr(),
                                            torch.cuda.current_stream().cuda_stream)
     assert st == _lib.OK
     torch.cuda.synchronize()
@@ -43,7 +43,7 @@ def test_hbm_probe_binding():
 def test_mfma_probe_runs_and_counts_its_operations():
     sink = _sink(torch.float32)
     flops = ctypes.c_double(0.0)
-    st = _lib.load().lmhead_probe_mfma_bf16(50, 1, sink.data_ptr(),
+    st = _lib.load_probes().lmhead_probe_mfma_bf16(50, 1, sink.data_ptr(),
                                             torch.cuda.current_stream().cuda_stream,
                                             ctypes.byref(flops))
     assert st == _lib.OK
