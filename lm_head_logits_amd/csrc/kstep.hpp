@@ -31,6 +31,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace lmhead {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -149,34 +151,26 @@ __device__ __forceinline__ float epilogue_v(float acc, float alpha, bool has_bia
   return t;
 }
 
-// One output element through a buffer resource: fp32, or bf16 / fp16
-// rounded to nearest even. Offsets past the resource are dropped by the
-// hardware.
-template <typename OutT>
-__device__ __forceinline__ void store_c(rsrc_t r, uint32_t voff, uint32_t soff, float t);
-
-// Logits are written with the streaming hint: they are not re-read by this
-// kernel, and keeping them out of the caches spares the next call's weight
-// stream (measured: the decode call after an M = 64 call ran 3% faster, the
-// M = 128 tiled call 4%).
+// Logits are written with the streaming hint by default: they are not
+// re-read by this kernel, and keeping them out of the caches spares the next
+// call's weight stream (measured: the M = 128 tiled call 7% faster than with
+// the default policy). The weight-streaming kernel, whose weight loads carry
+// the read-once hint themselves, writes with the default policy (spec-decode
+// draft M = 32: 104.5 against 106.5 µs).
 constexpr int STORE_POLICY = LOAD_STREAM;
 
-template <>
-__device__ __forceinline__ void store_c<float>(rsrc_t r, uint32_t voff, uint32_t soff, float t) {
-  __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, t), r, voff, soff,
-                                        STORE_POLICY);
-}
-
-template <>
-__device__ __forceinline__ void store_c<uint16_t>(rsrc_t r, uint32_t voff, uint32_t soff, float t) {
-  __builtin_amdgcn_raw_buffer_store_b16(bf16_rne(t), r, voff, soff, STORE_POLICY);
-}
-
-// fp16 logits: the conversion rounds to nearest even (the default mode).
-template <>
-__device__ __forceinline__ void store_c<_Float16>(rsrc_t r, uint32_t voff, uint32_t soff, float t) {
-  __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(uint16_t, (_Float16)t), r, voff, soff,
-                                        STORE_POLICY);
+// One output element through a buffer resource: fp32, or bf16 / fp16
+// rounded to nearest even (the fp16 conversion's default mode). Offsets past
+// the resource are dropped by the hardware.
+template <typename OutT, int POLICY = STORE_POLICY>
+__device__ __forceinline__ void store_c(rsrc_t r, uint32_t voff, uint32_t soff, float t) {
+  if constexpr (sizeof(OutT) == 4)
+    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, t), r, voff, soff, POLICY);
+  else if constexpr (std::is_same_v<OutT, _Float16>)
+    __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(uint16_t, (_Float16)t), r, voff, soff,
+                                          POLICY);
+  else
+    __builtin_amdgcn_raw_buffer_store_b16(bf16_rne(t), r, voff, soff, POLICY);
 }
 
 // An offset past any output resource (resources are < 1 GiB and scalar
@@ -191,7 +185,7 @@ constexpr uint32_t OFF_NONE = 0x80000000u;
 // Output element (rbase + 16 i + 4 lg + q, cbase + 16 j + li) of a row-major
 // [M, V] matrix. Rows past `rows` are dropped by the resource bound, columns
 // >= cend by an out-of-range offset; the bias is read once per column.
-template <int FM, int FN, typename OutT, typename Acc>
+template <int FM, int FN, int POLICY = STORE_POLICY, typename OutT, typename Acc>
 __device__ __forceinline__ void store_blocks(Acc &&acc, OutT *out, int64_t rbase, int64_t rows,
                                              int64_t cbase, int64_t cend, int64_t V,
                                              float alpha, const float *__restrict__ bias) {
@@ -217,8 +211,8 @@ __device__ __forceinline__ void store_blocks(Acc &&acc, OutT *out, int64_t rbase
     for (int i = 0; i < FM; ++i)
 #pragma unroll
       for (int q = 0; q < 4; ++q)
-        store_c<OutT>(r, voff, (uint32_t)((16 * i + q) * V * sizeof(OutT)),
-                      epilogue_v(acc(i, j)[q], alpha, has_bias, b));
+        store_c<OutT, POLICY>(r, voff, (uint32_t)((16 * i + q) * V * sizeof(OutT)),
+                              epilogue_v(acc(i, j)[q], alpha, has_bias, b));
   }
 }
 

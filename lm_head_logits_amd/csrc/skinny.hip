@@ -263,7 +263,8 @@ __global__ __launch_bounds__(64 * NW, NW >= 8 ? 1 : 2) void skinny_kernel(
   if (!active) return;
   const int64_t rows = M - m0 < 16 * R ? M - m0 : 16 * R;
   auto at = [&](int i, int j) -> f32x4 & { return acc[j][i]; };
-  if (out != nullptr) store_blocks<R, NB>(at, out, m0, rows, cb0 * 16, cend, V, alpha, bias);
+  if (out != nullptr)
+    store_blocks<R, NB, LOAD_DEFAULT>(at, out, m0, rows, cb0 * 16, cend, V, alpha, bias);
   if (part != nullptr) reduce_blocks<R, NB>(at, part, m0, rows, cb0 * 16, cend, V, alpha, bias);
 }
 
