@@ -42,6 +42,52 @@ __host__ __device__ constexpr bool korder_staggered(int64_t H, int64_t V) {
   return H % KORDER_STEP == 0 && H / KORDER_STEP > 1 && V > KORDER_COLS;
 }
 
+// Split of `ncb` vocabulary column blocks (16 weight rows each) of a head of
+// row length H over the waves of a weight-streaming kernel with `waves` waves
+// per work-group: `nvs` work-groups along V, each wave owning at most `nb`
+// consecutive blocks. The weight stream's bandwidth grows with the number of
+// CUs streaming, so the grid is about `slots` work-groups (one per CU; fewer
+// when V is small). When the head's K orders have several starts the blocks
+// are split group by group -- `kwg` work-groups per full group of `gblocks`
+// blocks, about in proportion to its blocks, the rest to the last -- so that
+// a work-group's columns share one start; otherwise one group of all blocks.
+// Within a group every wave owns floor or ceil of the mean (the kernels
+// derive their own range with split_cols below). Past nb_max blocks per wave
+// the grid grows instead. Host code.
+struct VSplit {
+  int64_t nvs;
+  int nb;
+  int64_t gblocks, kwg;
+};
+inline VSplit split_plan(int64_t ncb, int64_t H, int waves, int nb_max, int64_t slots) {
+  // work-groups that give `blocks` blocks at most nb per wave
+  auto need = [&](int64_t blocks, int64_t nb) { return (blocks + nb * waves - 1) / (nb * waves); };
+  if (!korder_staggered(H, ncb * 16) || ncb <= KORDER_BLOCKS) {
+    int64_t nvs = need(ncb, 1);  // at least one block per wave
+    if (nvs > slots) nvs = slots;
+    int64_t nb = (ncb + nvs * waves - 1) / (nvs * waves);
+    if (nb > nb_max) {
+      nb = nb_max;
+      nvs = need(ncb, nb);
+    }
+    return VSplit{nvs, (int)nb, ncb > 0 ? ncb : 1, nvs};
+  }
+  // groups of KORDER_BLOCKS blocks, the last one of lb
+  const int64_t gb = KORDER_BLOCKS, ng = (ncb + gb - 1) / gb, lb = ncb - (ng - 1) * gb;
+  auto clamp = [](int64_t v, int64_t lo, int64_t hi) { return v < lo ? lo : (v > hi ? hi : v); };
+  int64_t kf = clamp(slots * gb / ncb, 1, need(gb, 1));
+  int64_t kl = clamp((kf * lb + gb - 1) / gb, 1, need(lb, 1));
+  if ((ng - 1) * kf + kl > slots && kl > 1) --kl;  // never two work-groups on one CU
+  const int64_t nbf = (gb + kf * waves - 1) / (kf * waves), nbl = (lb + kl * waves - 1) / (kl * waves);
+  int64_t nb = nbf > nbl ? nbf : nbl;
+  if (nb > nb_max) {
+    nb = nb_max;
+    kf = need(gb, nb);
+    kl = need(lb, nb);
+  }
+  return VSplit{(ng - 1) * kf + kl, (int)nb, gb, kf};
+}
+
 // Split of ncb column blocks over a weight-streaming grid of nwg work-groups
 // of nw waves: the blocks come in groups of gblocks (KORDER_BLOCKS when the
 // starts are staggered, else all of them); each full group has kwg

@@ -54,23 +54,8 @@ hipError_t launch_kernel(void (*kernel)(P...), dim3 grid, dim3 block, hipStream_
 // Compute units of the current device (queried once per device).
 int device_cus();
 
-// Split of `ncb` vocabulary column blocks (16 weight rows each) of a head of
-// row length H over the waves of a weight-streaming kernel with `waves` waves
-// per work-group: `nvs` work-groups along V, each wave owning at most `nb`
-// consecutive blocks. The weight stream's bandwidth grows with the number of
-// CUs streaming, so the grid is about `per_cu` work-groups per CU (fewer when
-// V is small). When the head's K orders have several starts (korder.hpp) the
-// blocks are split group by group -- `kwg` work-groups per full group of
-// `gblocks` blocks, about in proportion to its blocks, the rest to the last --
-// so that a work-group's columns share one start; otherwise one group of all
-// blocks. Within a group every wave owns floor or ceil of the mean (the
-// kernels derive their own range with split_cols). Past nb_max blocks per
-// wave the grid grows instead.
-struct VSplit {
-  int64_t nvs;
-  int nb;
-  int64_t gblocks, kwg;
-};
+// The vocabulary split of a weight-streaming launch (split_plan in
+// korder.hpp) for `per_cu` work-groups per compute unit of the current device.
 VSplit vsplit(int64_t ncb, int64_t H, int waves, int nb_max, int per_cu = 1);
 
 // Folds the partials of each row into its (max, argmax, sum of exp(x - max)).

@@ -88,33 +88,7 @@ int device_cus() {
 }
 
 VSplit vsplit(int64_t ncb, int64_t H, int waves, int nb_max, int per_cu) {
-  const int64_t slots = (int64_t)device_cus() * per_cu;
-  // work-groups that give `blocks` blocks at most nb per wave
-  auto need = [&](int64_t blocks, int64_t nb) { return (blocks + nb * waves - 1) / (nb * waves); };
-  if (!korder_staggered(H, ncb * 16) || ncb <= KORDER_BLOCKS) {
-    int64_t nvs = need(ncb, 1);  // at least one block per wave
-    if (nvs > slots) nvs = slots;
-    int64_t nb = (ncb + nvs * waves - 1) / (nvs * waves);
-    if (nb > nb_max) {
-      nb = nb_max;
-      nvs = need(ncb, nb);
-    }
-    return VSplit{nvs, (int)nb, ncb > 0 ? ncb : 1, nvs};
-  }
-  // groups of KORDER_BLOCKS blocks, the last one of lb
-  const int64_t gb = KORDER_BLOCKS, ng = (ncb + gb - 1) / gb, lb = ncb - (ng - 1) * gb;
-  auto clamp = [](int64_t v, int64_t lo, int64_t hi) { return v < lo ? lo : (v > hi ? hi : v); };
-  int64_t kf = clamp(slots * gb / ncb, 1, need(gb, 1));
-  int64_t kl = clamp((kf * lb + gb - 1) / gb, 1, need(lb, 1));
-  if ((ng - 1) * kf + kl > slots && kl > 1) --kl;  // never two work-groups on one CU
-  const int64_t nbf = (gb + kf * waves - 1) / (kf * waves), nbl = (lb + kl * waves - 1) / (kl * waves);
-  int64_t nb = nbf > nbl ? nbf : nbl;
-  if (nb > nb_max) {
-    nb = nb_max;
-    kf = need(gb, nb);
-    kl = need(lb, nb);
-  }
-  return VSplit{(ng - 1) * kf + kl, (int)nb, gb, kf};
+  return split_plan(ncb, H, waves, nb_max, (int64_t)device_cus() * per_cu);
 }
 
 lmhead_status rowreduce_check(const void *hidden, int64_t M, int64_t H, const void *W, int64_t V,
