@@ -213,10 +213,16 @@ __device__ __forceinline__ void transpose4(uint32_t &x0, uint32_t &x1, uint32_t 
 // 16 bytes of that chunk. The next group's scales are loaded at the group's
 // last chunk, into the registers just read.
 //
-// With the K-steps the kernel is bound by the dequantisation's VALU work
-// (about 2 instructions per weight: counters show the VALU busy about half of
-// the cycles), which overlaps the stream only in part: a variant with the
-// dequantisation replaced by one instruction per K-step ran in 39 µs.
+// The kernel is bound by its waves' instruction streams, not by the weight
+// stream. Timing-only copies (M = 1, H = 2048, V = 151936, one MI355X): with
+// every code load hitting L2 it ran as fast as with the codes from HBM
+// (42.6 against 42.8 µs); without the dequantisation (about 2 VALU
+// instructions per weight) in 31 µs; without that and the direct loads in
+// 22 µs, and that skeleton fell to 9-12 µs when either its MFMAs or its lane
+// transposes were removed: transposes interleaved with MFMAs stall. Reading
+// the codes with eight 4-byte LDS reads instead of transposing them was
+// slower. A wave may own fewer blocks than NB; its K-steps for the others
+// are skipped (6-8% at this shape).
 //
 // Issue order: at the read of unit v (and in the prologue for v < 0) a
 // "batch": unit v + NSL's two direct loads; the hidden loads of chunk
@@ -258,6 +264,7 @@ __global__ __launch_bounds__(64 * NW, 1) void nvfp4_ring_kernel(
                                  gblocks, kwg, H);
   const int64_t cb0 = wc.cb0, cb1 = wc.cb1;
   const bool active = cb1 > cb0;
+  const int nbw = (int)(cb1 - cb0);  // blocks this wave owns (<= NB)
   const int64_t cend = cb1 * 16 < V ? cb1 * 16 : V;
 
   const int64_t HC = H / 2, HS = H / 16;
@@ -409,8 +416,13 @@ __global__ __launch_bounds__(64 * NW, 1) void nvfp4_ring_kernel(
 #pragma unroll
       for (int r = 0; r < R; ++r) acc[J][r] = kstep(acc[J][r], a[r], b);
     };
-    static_for<4>([&](auto tc) { kstep_t(tc); });
-    if (!half) static_for<4>([&](auto tc) { kstep_t(std::integral_constant<int, 4 + decltype(tc)::value>{}); });
+    // a wave may own fewer blocks than NB: the slot of a block it does not
+    // own holds zeros (its loads are still issued, to keep the schedule's
+    // counts), and its K-steps are skipped (a wave-uniform branch)
+    if (J < nbw) {
+      static_for<4>([&](auto tc) { kstep_t(tc); });
+      if (!half) static_for<4>([&](auto tc) { kstep_t(std::integral_constant<int, 4 + decltype(tc)::value>{}); });
+    }
     if constexpr (J == NB - 1) {
       wait_vm<S::wait_hidden(P)>();
       store_hidden(hring[(P / NB + 1) % NHR], BUF ^ 1);
