@@ -111,6 +111,7 @@ __global__ __launch_bounds__(64 * NW, NW >= 8 ? 1 : 2) void skinny_kernel(
                                  gblocks, kwg, H);
   const int64_t cb0 = wc.cb0, cb1 = wc.cb1;
   const bool active = cb1 > cb0;  // wave-uniform
+  const int nbw = (int)(cb1 - cb0);  // blocks this wave owns (<= NB)
   const int64_t cend = cb1 * 16 < V ? cb1 * 16 : V;  // end of this wave's columns
 
   // Weight: one buffer resource per wave over its rows [16 cb0, cend)
@@ -219,13 +220,20 @@ __global__ __launch_bounds__(64 * NW, NW >= 8 ? 1 : 2) void skinny_kernel(
         a1[r] = hs[BUF][hslot(16 * r + li, 4 + lg)];
       }
     }
-    const u32x4 b0 = wl[wave * SK_WSLOT + wslot(li, lg)];
+    // A wave may own fewer blocks than NB: the slot of a block it does not
+    // own holds zeros (its loads are still issued, to keep the schedule's
+    // counts); its K-steps are skipped (wave-uniform). At M = 64, H = 2048,
+    // V = 151936 (up to 3 blocks a wave, most waves 2) this took the call from
+    // 116 to 104 µs.
+    if (J < nbw) {
+      const u32x4 b0 = wl[wave * SK_WSLOT + wslot(li, lg)];
 #pragma unroll
-    for (int r = 0; r < R; ++r) acc[J][r] = kstep<F16>(acc[J][r], a0[r], b0);
-    if (!(odd_tail && c == nchunks - 1)) {  // wave-uniform
-      const u32x4 b1 = wl[wave * SK_WSLOT + wslot(li, 4 + lg)];
+      for (int r = 0; r < R; ++r) acc[J][r] = kstep<F16>(acc[J][r], a0[r], b0);
+      if (!(odd_tail && c == nchunks - 1)) {  // wave-uniform
+        const u32x4 b1 = wl[wave * SK_WSLOT + wslot(li, 4 + lg)];
 #pragma unroll
-      for (int r = 0; r < R; ++r) acc[J][r] = kstep<F16>(acc[J][r], a1[r], b1);
+        for (int r = 0; r < R; ++r) acc[J][r] = kstep<F16>(acc[J][r], a1[r], b1);
+      }
     }
     // Refill the slot with unit u + NSL. A direct load writes LDS on its own
     // path, not behind the wave's earlier ds_reads: wait until they have
