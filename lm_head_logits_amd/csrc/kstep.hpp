@@ -302,13 +302,16 @@ __device__ __forceinline__ void store_rows_lds(Acc &&acc, OutT *out, float *stg,
 // its lowest column and sums 0, and contributes nothing to a row that has a
 // finite logit. +inf and NaN logits are outside the contract.
 //
-// A block's partial depends only on the block's 16 logits and their lane
-// positions (column c0 + li in lane 16 g + li): the maximum and its column
-// are exact, and the sum is a fixed butterfly over the 16 lanes, in which
-// both partners of every step add the same two values (the same bits). So the
-// partials, and the combined row results, are the same whichever kernel ran
-// and however many rows the call had. (When the maximum is a zero present
-// with both signs, the sign of the zero stored is the hardware maximum's.)
+// A block's partial depends only on the block's 16 logits and their column
+// positions: the maximum and its column are exact, and the sum has one fixed
+// order. Each row's 16 logits pass through a wave-private LDS area so that
+// four lanes hold four consecutive columns each: a lane sums its four terms
+// in column order, then the four lanes meet in a butterfly (pairs, then
+// quads), in which both partners of every step add the same two values (the
+// same bits). So the partials, and the combined row results, are the same
+// whichever kernel ran and however many rows the call had. (When the
+// maximum is a zero present with both signs, the sign of the zero stored is
+// the hardware maximum's.)
 //
 // Record of row m, block cb at part[m * ncb + cb] (ncb = ceil(V / 16)).
 // ---------------------------------------------------------------------------
@@ -330,17 +333,10 @@ __device__ __forceinline__ void max_lowest(float &m, int &mi, float om, int oi) 
   }
 }
 
-// Butterfly over the 16 lanes of a DPP row (lanes 16 g .. 16 g + 15) by data
-// movement within the row: partner lane l ^ 1, l ^ 2 (quad permutations),
-// then the mirror inside 8 lanes and inside 16 lanes. The four steps pair the
-// same lanes' values as an xor butterfly 1, 2, 4, 8 does (pairs, quads,
-// halves, rows), and each step combines two values with an operation for
-// which both partners compute the same bits, so every lane ends with the
-// same result.
-constexpr int DPP_QUAD_SWAP1 = 0xB1;        // quad_perm [1, 0, 3, 2]
-constexpr int DPP_QUAD_SWAP2 = 0x4E;        // quad_perm [2, 3, 0, 1]
-constexpr int DPP_ROW_HALF_MIRROR = 0x141;  // lane i <-> 7 - i within 8
-constexpr int DPP_ROW_MIRROR = 0x140;       // lane i <-> 15 - i within 16
+// Butterfly steps over the four lanes of a quad (lanes 4 r .. 4 r + 3):
+// partner lane l ^ 1, then l ^ 2.
+constexpr int DPP_QUAD_SWAP1 = 0xB1;  // quad_perm [1, 0, 3, 2]
+constexpr int DPP_QUAD_SWAP2 = 0x4E;  // quad_perm [2, 3, 0, 1]
 
 template <int CTRL>
 __device__ __forceinline__ int dpp(int v) {
@@ -351,61 +347,88 @@ __device__ __forceinline__ float dpp(float v) {
   return __builtin_bit_cast(float, dpp<CTRL>(__builtin_bit_cast(int, v)));
 }
 
-// Largest value over the row's 16 lanes. Equal values of opposite zero sign
-// may come back as either zero; nothing below depends on which.
-__device__ __forceinline__ float row16_max(float v) {
-  v = fmaxf(v, dpp<DPP_QUAD_SWAP1>(v));
-  v = fmaxf(v, dpp<DPP_QUAD_SWAP2>(v));
-  v = fmaxf(v, dpp<DPP_ROW_HALF_MIRROR>(v));
-  return fmaxf(v, dpp<DPP_ROW_MIRROR>(v));
-}
-__device__ __forceinline__ int row16_min(int v) {
-  v = min(v, dpp<DPP_QUAD_SWAP1>(v));
-  v = min(v, dpp<DPP_QUAD_SWAP2>(v));
-  v = min(v, dpp<DPP_ROW_HALF_MIRROR>(v));
-  return min(v, dpp<DPP_ROW_MIRROR>(v));
-}
-__device__ __forceinline__ float row16_sum(float v) {
-  v = __fadd_rn(v, dpp<DPP_QUAD_SWAP1>(v));
-  v = __fadd_rn(v, dpp<DPP_QUAD_SWAP2>(v));
-  v = __fadd_rn(v, dpp<DPP_ROW_HALF_MIRROR>(v));
-  return __fadd_rn(v, dpp<DPP_ROW_MIRROR>(v));
-}
-
 // e^x as 2^(x log2 e) (the hardware exp2 of a rounded product).
 __device__ __forceinline__ float exp_fast(float x) { return __expf(x); }
 
+// Floats of LDS one wave needs for reduce_blocks (16 rows of 16 logits,
+// row stride 20: the writes of one register, rows 4 g + q at lanes 16 g + i,
+// land in distinct banks, and each row's four 16-byte pieces stay aligned).
+constexpr int RED_STRIDE = 20;
+constexpr int RED_STG_FLOATS = 16 * RED_STRIDE;
+
+// The row partials of a wave's FM x FN blocks (rows rbase.., columns cbase..,
+// columns from cend on absent). `stg`: RED_STG_FLOATS floats of LDS of this
+// wave's own, 16-byte aligned, free for the duration.
 template <int FM, int FN, typename Acc>
-__device__ __forceinline__ void reduce_blocks(Acc &&acc, RowPart *__restrict__ part, int64_t rbase,
-                                              int64_t rows, int64_t cbase, int64_t cend,
-                                              int64_t V, float alpha,
+__device__ __forceinline__ void reduce_blocks(Acc &&acc, RowPart *__restrict__ part, float *stg,
+                                              int64_t rbase, int64_t rows, int64_t cbase,
+                                              int64_t cend, int64_t V, float alpha,
                                               const float *__restrict__ bias) {
   const int lane = threadIdx.x & 63;
   const int li = lane & 15, lg = lane >> 4;
+  const int rr = lane >> 2, t = lane & 3;  // reading side: row rr, columns 4 t .. 4 t + 3
   const int64_t ncb = (V + 15) / 16;
   const bool has_bias = bias != nullptr;
+  constexpr float NEG_INF = -__builtin_inff();
+  // every block's bias first: its loads in flight together, not one
+  // round trip per block
+  float bj[FN];
 #pragma unroll
   for (int j = 0; j < FN; ++j) {
-    if (cbase + 16 * j >= cend) break;  // wave-uniform: this and later blocks have no column
     const int64_t col = cbase + 16 * j + li;
-    const bool ok = col < cend;
-    const float b = (has_bias && ok) ? bias[col] : 0.0f;
-    const int64_t cb = (cbase >> 4) + j;
-#pragma unroll
-    for (int i = 0; i < FM; ++i)
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const float t = ok ? epilogue_v(acc(i, j)[q], alpha, has_bias, b) : -__builtin_inff();
-        const float m = row16_max(t);
-        const int mi = row16_min(ok && t == m ? (int)col : 0x7FFFFFFF);
-        // a block whose logits are all -inf (a masked vocabulary range) has
-        // m = -inf and sums nothing: exp(t - m) would be exp(-inf + inf)
-        const bool live = ok && m != -__builtin_inff();
-        const float e = row16_sum(live ? exp_fast(__fsub_rn(t, m)) : 0.0f);
-        const int r = 16 * i + 4 * lg + q;  // row within the wave's rows
-        if (li == q && r < rows) part[(rbase + r) * ncb + cb] = RowPart{m, e, mi, 0};
-      }
+    bj[j] = (has_bias && col < cend) ? bias[col] : 0.0f;
   }
+  // columns fit 32 bits (V <= 2^20 by the shape contract); this lane's record
+  // slot for block 0 of its row
+  const int cw = (int)cbase + 4 * t;  // the reading lane's first column in block 0
+  RowPart *prow = part + (rbase + rr) * ncb + (cbase >> 4);
+  const int nok = (int)(cend - cbase);  // columns present from cbase on
+  // the body once with and once without the bias add (a uniform choice)
+  auto run = [&](auto hb) {
+    constexpr bool HB = decltype(hb)::value;
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      if (16 * j >= nok) break;  // wave-uniform: this and later blocks have no column
+      const bool ok = 16 * j + li < nok;
+#pragma unroll
+      for (int i = 0; i < FM; ++i) {
+        // the block's logits, row-major (absent columns -inf)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const float tv = epilogue_v(acc(i, j)[q], alpha, HB, bj[j]);
+          stg[(4 * lg + q) * RED_STRIDE + li] = ok ? tv : NEG_INF;
+        }
+        __builtin_amdgcn_wave_barrier();  // other lanes' values: LDS keeps a wave's order
+        const f32x4 v = *reinterpret_cast<const f32x4 *>(stg + rr * RED_STRIDE + 4 * t);
+        __builtin_amdgcn_wave_barrier();  // this read before the next block's writes
+        float m = fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3]));
+        m = fmaxf(m, dpp<DPP_QUAD_SWAP1>(m));
+        m = fmaxf(m, dpp<DPP_QUAD_SWAP2>(m));
+        // lowest column holding m: the absent columns (-inf) come after every
+        // present one, and a block has a present column, so one of those wins
+        int mi = 0x7FFFFFFF;
+#pragma unroll
+        for (int k = 3; k >= 0; --k)
+          if (v[k] == m) mi = cw + 16 * j + k;
+        mi = min(mi, dpp<DPP_QUAD_SWAP1>(mi));
+        mi = min(mi, dpp<DPP_QUAD_SWAP2>(mi));
+        // a block whose logits are all -inf (a masked vocabulary range) has
+        // m = -inf and sums nothing: its terms are taken against 0 instead
+        // (exp(-inf - 0) = 0), never exp(-inf + inf)
+        const float mz = m == NEG_INF ? 0.0f : m;
+        float e = exp_fast(__fsub_rn(v[0], mz));
+#pragma unroll
+        for (int k = 1; k < 4; ++k) e = __fadd_rn(e, exp_fast(__fsub_rn(v[k], mz)));
+        e = __fadd_rn(e, dpp<DPP_QUAD_SWAP1>(e));
+        e = __fadd_rn(e, dpp<DPP_QUAD_SWAP2>(e));
+        if (t == 0 && 16 * i + rr < rows) prow[16 * i * ncb + j] = RowPart{m, e, mi, 0};
+      }
+    }
+  };
+  if (has_bias)
+    run(std::true_type{});
+  else
+    run(std::false_type{});
 }
 
 }  // namespace lmhead

@@ -273,7 +273,15 @@ __global__ __launch_bounds__(64 * NW, NW >= 8 ? 1 : 2) void skinny_kernel(
   auto at = [&](int i, int j) -> f32x4 & { return acc[j][i]; };
   if (out != nullptr)
     store_blocks<R, NB, LOAD_DEFAULT>(at, out, m0, rows, cb0 * 16, cend, V, alpha, bias);
-  if (part != nullptr) reduce_blocks<R, NB>(at, part, m0, rows, cb0 * 16, cend, V, alpha, bias);
+  if (part != nullptr) {
+    // the wave's ring slot 0 stages the reduction: every direct load that
+    // could still write it (the ring's loads of nothing past the end
+    // included) has landed first
+    wait_vm<0>();
+    float *stg = reinterpret_cast<float *>(&Wl0[wave * SK_WSLOT]);
+    static_assert(SK_WSLOT * 4 >= RED_STG_FLOATS, "reduction staging fits a ring slot");
+    reduce_blocks<R, NB>(at, part, stg, m0, rows, cb0 * 16, cend, V, alpha, bias);
+  }
 }
 
 template <int R, int NB, bool F16, typename OutT, int NW, int NSL>

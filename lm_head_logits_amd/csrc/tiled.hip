@@ -307,34 +307,33 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void tiled_kernel(TiledArgs args) 
   const int64_t rows = M - rb < SM ? M - rb : SM;
   const int64_t cb = n0 + wn * SN;
   auto at = [&](int i, int j) -> f32x4 & { return acc[i][j]; };
+  // The stage buffers are free once every wave has read its last stage; each
+  // wave then stages its epilogue in an LDS area of its own.
+  constexpr int STG = stage_rows_floats<FN>();
+  constexpr int PER_A = TM * TL_PPR * 16 / (4 * STG), PER_B = TN * TL_PPR * 16 / (4 * STG);
+  static_assert(2 * PER_A + 2 * PER_B >= NW, "epilogue staging fits the stage buffers");
+  static_assert(STG >= RED_STG_FLOATS, "the reduction's staging fits the logits' area");
+  auto wave_stg = [&]() -> float * {
+    int w = wave;
+    if (w < PER_A) return reinterpret_cast<float *>(As0) + w * STG;
+    if ((w -= PER_A) < PER_A) return reinterpret_cast<float *>(As1) + w * STG;
+    if ((w -= PER_A) < PER_B) return reinterpret_cast<float *>(Bs0) + w * STG;
+    return reinterpret_cast<float *>(Bs1) + (w - PER_B) * STG;
+  };
   if (!RED || out != nullptr) {
-    // Logits through LDS in whole rows (the stage buffers are free once every
-    // wave has read its last stage); waves whose columns run past V, or rows
-    // not 16-byte aligned (V % 8 != 0), store block by block.
-    constexpr int STG = stage_rows_floats<FN>();
-    constexpr int PER_A = TM * TL_PPR * 16 / (4 * STG), PER_B = TN * TL_PPR * 16 / (4 * STG);
-    static_assert(2 * PER_A + 2 * PER_B >= NW, "epilogue staging fits the stage buffers");
+    // Logits in whole rows; waves whose columns run past V, or rows not
+    // 16-byte aligned (V % 8 != 0), store block by block.
     __syncthreads();
-    if (V % 8 == 0 && cb + SN <= V) {
-      int w = wave;
-      float *stg;
-      if (w < PER_A) {
-        stg = reinterpret_cast<float *>(As0) + w * STG;
-      } else if ((w -= PER_A) < PER_A) {
-        stg = reinterpret_cast<float *>(As1) + w * STG;
-      } else if ((w -= PER_A) < PER_B) {
-        stg = reinterpret_cast<float *>(Bs0) + w * STG;
-      } else {
-        w -= PER_B;
-        stg = reinterpret_cast<float *>(Bs1) + w * STG;
-      }
-      store_rows_lds<FM, FN>(at, out, stg, rb, rows, cb, V, alpha, bias);
-    } else {
+    if (V % 8 == 0 && cb + SN <= V)
+      store_rows_lds<FM, FN>(at, out, wave_stg(), rb, rows, cb, V, alpha, bias);
+    else
       store_blocks<FM, FN>(at, out, rb, rows, cb, V, V, alpha, bias);
-    }
   }
-  if constexpr (RED)
-    reduce_blocks<FM, FN>(at, static_cast<RowPart *>(args.part), rb, rows, cb, V, V, alpha, bias);
+  if constexpr (RED) {
+    if (out == nullptr) __syncthreads();
+    reduce_blocks<FM, FN>(at, static_cast<RowPart *>(args.part), wave_stg(), rb, rows, cb, V, V,
+                          alpha, bias);
+  }
 }
 
 template <int TM, int TN, int WM, int WN, bool NV, bool F16, typename OutT, int TAIL>
