@@ -335,8 +335,10 @@ __device__ __forceinline__ void max_lowest(float &m, int &mi, float om, int oi) 
 
 // Butterfly steps over the four lanes of a quad (lanes 4 r .. 4 r + 3):
 // partner lane l ^ 1, then l ^ 2.
-constexpr int DPP_QUAD_SWAP1 = 0xB1;  // quad_perm [1, 0, 3, 2]
-constexpr int DPP_QUAD_SWAP2 = 0x4E;  // quad_perm [2, 3, 0, 1]
+constexpr int DPP_QUAD_SWAP1 = 0xB1;        // quad_perm [1, 0, 3, 2]
+constexpr int DPP_QUAD_SWAP2 = 0x4E;        // quad_perm [2, 3, 0, 1]
+constexpr int DPP_ROW_HALF_MIRROR = 0x141;  // lane i <-> 7 - i within 8
+constexpr int DPP_ROW_MIRROR = 0x140;       // lane i <-> 15 - i within 16
 
 template <int CTRL>
 __device__ __forceinline__ int dpp(int v) {

@@ -13,8 +13,9 @@
 // Order: work-group = one row, RC_THREADS threads; thread t folds blocks t,
 // t + RC_THREADS, t + 2 RC_THREADS, ... in ascending order (their loads are
 // issued RC_BATCH at a time, ahead of the folds), then the 64 lanes of a wave
-// meet in an xor butterfly and the waves' results in a second xor butterfly
-// over RC_WAVES lanes. Every fold is symmetric (both partners of a butterfly
+// meet in a butterfly (DPP steps within each 16-lane row, then xor 16 and
+// 32) and the waves' results in a 16-lane DPP butterfly. Every fold is
+// symmetric (both partners of a butterfly
 // step compute the same bits), and the order depends only on V, so a row's
 // result does not depend on M or on which GEMM kernel wrote the partials.
 #include "kstep.hpp"
@@ -53,6 +54,23 @@ __device__ __forceinline__ RowAcc shfl_xor(RowAcc a, int d) {
   return RowAcc{__shfl_xor(a.m, d), __shfl_xor(a.s, d), __shfl_xor(a.i, d)};
 }
 
+// The partner's RowAcc within a 16-lane row by DPP (no LDS round trip).
+template <int CTRL>
+__device__ __forceinline__ RowAcc dpp_acc(RowAcc a) {
+  return RowAcc{dpp<CTRL>(a.m), dpp<CTRL>(a.s), dpp<CTRL>(a.i)};
+}
+
+// Butterfly over the 16 lanes of each row: partner lane l ^ 1, l ^ 2 (quad
+// permutations), then the mirror inside 8 lanes and inside 16 lanes -- the
+// same pairs of groups an xor butterfly 4, 8 meets, so every lane ends with
+// the row's fold and both partners of each step fold the same two values.
+__device__ __forceinline__ RowAcc row16_fold(RowAcc a) {
+  a = fold(a, dpp_acc<DPP_QUAD_SWAP1>(a));
+  a = fold(a, dpp_acc<DPP_QUAD_SWAP2>(a));
+  a = fold(a, dpp_acc<DPP_ROW_HALF_MIRROR>(a));
+  return fold(a, dpp_acc<DPP_ROW_MIRROR>(a));
+}
+
 constexpr RowAcc EMPTY{-__builtin_inff(), 0.0f, 0x7FFFFFFF};
 
 __global__ __launch_bounds__(RC_THREADS) void row_combine_kernel(
@@ -71,16 +89,17 @@ __global__ __launch_bounds__(RC_THREADS) void row_combine_kernel(
 #pragma unroll
     for (int k = 0; k < RC_BATCH; ++k) a = fold(a, RowAcc{v[k].m, v[k].s, v[k].i});
   }
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) a = fold(a, shfl_xor(a, d));
+  a = row16_fold(a);
+  a = fold(a, shfl_xor(a, 16));
+  a = fold(a, shfl_xor(a, 32));
   __shared__ RowAcc w[RC_WAVES];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   if (lane == 0) w[wave] = a;
   __syncthreads();
   if (wave == 0) {
     a = lane < RC_WAVES ? w[lane] : EMPTY;
-#pragma unroll
-    for (int d = 1; d < RC_WAVES; d <<= 1) a = fold(a, shfl_xor(a, d));
+    static_assert(RC_WAVES == 16, "the waves' results meet within one 16-lane row");
+    a = row16_fold(a);
     if (lane == 0) {
       row_max[row] = a.m;
       row_argmax[row] = a.i;

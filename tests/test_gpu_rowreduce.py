@@ -120,6 +120,28 @@ def test_ties_across_blocks_waves_and_tiles():
     check_rowreduce_self(_np(mx), _np(am), _np(se), plain)
 
 
+@pytest.mark.parametrize("path", PATHS)
+def test_ties_inside_one_block(path):
+    # Ties among columns of one 16-column block: within one lane's four
+    # columns (4t .. 4t + 3) and across the four lanes that share a row of the
+    # block, and a whole block of equal logits; integer inputs keep every
+    # logit exact, so the lowest tied column must win in every row.
+    M, H, V = 20, 64, 4133
+    say(f"rowreduce ties inside one block via {path}")
+    h = wl.int_hidden(9, M, H)
+    W = wl.int_weight(9, V, H, -1, 1)
+    hv = oracle.bf16_to_f64(h)
+    top = f32_bits_to_bf16_bits_exact((np.sign(hv[0]) * 4).astype(np.float32))
+    for c in (1030, 1031, 1033, 1037, 1045):       # block 64: lanes 1, 2, 3; one lane's pair
+        W[c] = top
+    W[3200:3216] = f32_bits_to_bf16_bits_exact((np.sign(hv[1]) * 4).astype(np.float32))
+    mx, am, se, _ = L.logits_rowreduce(bf16_dev(h), bf16_dev(W), 0.25, path=path)
+    am = _np(am)
+    assert int(am[0]) == 1030 and int(am[1]) == 3200, (int(am[0]), int(am[1]))
+    plain = host_f32(L.logits(bf16_dev(h), bf16_dev(W), 0.25, path=path))
+    check_rowreduce_self(_np(mx), am, _np(se), plain)
+
+
 def test_rows_invariant_across_counts_and_order():
     rng = np.random.default_rng(11)
     M, H, V = 130, 128, 20000
