@@ -164,6 +164,45 @@ def bench_decode(torch, L, wl, dev, warmup, steps):
             "hd": hd, "Wd": Wd}
 
 
+def bench_tiny(torch, L, wl, dev, warmup, steps):
+    """The tiny head (M = 4, H = 256, V = 4096, fp32 logits): 2 MB of weight,
+    held in L2 between calls, so a call is bound by launch and ramp-up, not
+    by HBM; reported in µs per call with its fraction of the HBM roofline
+    for completeness."""
+    w = wl.TINY
+    log("tiny: generating inputs")
+    h, W = wl.hidden(w), wl.weight(w)
+    hd, Wd = to_dev_bf16(torch, h, dev), to_dev_bf16(torch, W, dev)
+    M = w.Ms[0]
+    out = torch.empty((M, w.V), dtype=torch.float32, device=dev)
+    _, _, per = timed_calls(torch, [lambda: L.logits(hd, Wd, w.alphas[0], None, torch.float32,
+                                                     out=out)], warmup, steps)
+    us = 1e3 * float(np.mean(per[0]))
+    by = bytes_bf16(M, w.H, w.V, 4, False)
+    # The same calls replayed from a HIP graph (the entry points allocate and
+    # synchronise nothing, so they can be captured): the per-call time without
+    # the host's launch overhead between calls.
+    calls = 20
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        L.logits(hd, Wd, w.alphas[0], None, torch.float32, out=out)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(calls):
+            L.logits(hd, Wd, w.alphas[0], None, torch.float32, out=out)
+    _, _, gper = timed_calls(torch, [g.replay], max(1, warmup // 5), max(2, steps // 5))
+    us_graph = 1e3 * float(np.mean(gper[0])) / calls
+    return {"M": M, "H": w.H, "V": w.V, "us_avg": round(us, 2),
+            "us_min": round(1e3 * float(np.min(per[0])), 2),
+            "us_per_call_graph_replay": round(us_graph, 2), "GBps": round(by / us / 1e3, 1),
+            "roofline_us": round(by / HBM_PEAK_GBPS / 1e3, 3),
+            "frac_hbm": round(by / us / 1e3 / HBM_PEAK_GBPS, 4),
+            "bound": "launch (the weight stays in L2)"}
+
+
 def bench_shard(torch, L, w, hd, Wd, warmup, steps, shards=8, copies=4):
     """The decode head's one-GPU share when the vocabulary is split over
     `shards` GPUs (V/8 = 16032 rows, 131 MB): `copies` distinct row ranges of
@@ -501,7 +540,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--only", choices=["decode", "prefill", "spec", "nvfp4", "f16", "rowreduce",
+    ap.add_argument("--only", choices=["decode", "tiny", "prefill", "spec", "nvfp4", "f16", "rowreduce",
                                        "quantize", "copy", "probes", "libgemm", "all"],
                     default="all",
                     help="run one workload only (for profiling; 'copy' is the HBM counter "
@@ -523,7 +562,8 @@ def main():
     extra = {}
     if args.only != "all" and args.only != "decode":
         # a single non-headline workload, for profiling: print its numbers only
-        fn = {"prefill": lambda: bench_prefill(torch, L, wl, dev, args.warmup, args.steps),
+        fn = {"tiny": lambda: bench_tiny(torch, L, wl, dev, args.warmup, args.steps),
+              "prefill": lambda: bench_prefill(torch, L, wl, dev, args.warmup, args.steps),
               "spec": lambda: bench_spec(torch, L, wl, dev, args.warmup, args.steps),
               "nvfp4": lambda: bench_nvfp4(torch, L, wl, dev, args.warmup, args.steps),
               "f16": lambda: bench_f16(torch, L, wl, dev, args.warmup, args.steps),
@@ -540,6 +580,8 @@ def main():
                                                args.warmup, args.steps)
     del dec["hd"], dec["Wd"]
     torch.cuda.empty_cache()
+    if run("tiny"):
+        extra["tiny"] = bench_tiny(torch, L, wl, dev, args.warmup, args.steps)
     if run("prefill"):
         extra["prefill"] = bench_prefill(torch, L, wl, dev, args.warmup, max(5, args.steps // 5))
         torch.cuda.empty_cache()
