@@ -301,6 +301,19 @@ def bench_nvfp4(torch, L, wl, dev, warmup, steps, copies=4):
                        "TFLOPs": round(f / us / 1e6, 1), "roofline_us": round(roof, 2),
                        "frac_roofline": round(roof / us, 4)}
     del cs, ss
+    # The ceiling for streaming this many bytes at all: the HBM read probe on
+    # buffers of the M = 1 call's size, rotated like the heads (so none is
+    # served from the MALL): the best fraction of the roofline any kernel
+    # that reads the head once can reach at this size.
+    nb = (bytes_nvfp4(1, w.H, w.V) + 15) // 16 * 16
+    bufs = [torch.empty(nb // 2, dtype=torch.bfloat16, device=dev).normal_() for _ in range(copies)]
+    _, _, pp = timed_calls(torch, [rotating([(lambda b=b: L.probe_hbm_read(b)) for b in bufs])],
+                           warmup * copies, steps * copies)
+    probe_us = 1e3 * float(np.mean(pp))
+    res["hbm_read_probe_same_bytes"] = {"bytes": nb, "us_avg": round(probe_us, 2),
+                                        "GBps": round(nb / probe_us / 1e3, 1),
+                                        "frac_of_m1_roofline": round(res["1"]["roofline_us"] / probe_us, 4)}
+    del bufs
     # Side by side: the bf16 entry point on a bf16 head of the same shape
     # (the same logits type), at the row count the tiled kernel serves.
     Wb = (0.02 * torch.randn(w.V, w.H, device=dev)).to(torch.bfloat16)
