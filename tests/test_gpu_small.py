@@ -294,6 +294,54 @@ def test_nvfp4_misaligned_scales_take_the_generic_kernel():
     assert torch.equal(a.view(torch.int16), b.view(torch.int16))
 
 
+# Hidden rows of extreme magnitude through the M <= 32 NVFP4 kernel: typical
+# rows, rows scaled by 2^-60, 2^10 and 2^-100, zeros and signed zeros, one
+# value of 1e-30 beside O(1) values, one of 40000, one bf16 subnormal. The
+# bits must be those of the bf16 chain on the dequantised head (both bf16
+# paths) and within the oracle's bound.
+_EXTREME_CASES = ("normal", "x2^-60", "x2^10", "zeros", "signed_zero", "tiny", "big", "subnormal",
+               "x2^-100")
+
+
+@pytest.mark.parametrize("M", [1, 5, 20, 32])
+@pytest.mark.parametrize("case", _EXTREME_CASES)
+def test_nvfp4_ring_extreme_hidden_equals_bf16_chain(M, case):
+    H, V = 1024, 700
+    rng = np.random.default_rng(7 * M + len(case))
+    say(f"nvfp4 ring extreme hidden {case} M={M}")
+    x = rng.normal(0, 1, (M, H))
+    if case == "x2^-60":
+        x = x * 2.0 ** -60
+    elif case == "x2^10":
+        x = x * 2.0 ** 10
+    elif case == "x2^-100":
+        x = x * 2.0 ** -100
+    elif case == "zeros":
+        x[:] = 0.0
+        x[M // 2, 3] = 1.5
+    elif case == "signed_zero":
+        x[:, ::3] = -0.0
+        x[:, 1::3] = 0.0
+    elif case == "tiny":
+        x[M - 1, H // 2] = 1e-30
+    elif case == "big":
+        x[0, 5] = 40000.0
+    h = oracle.f32_to_bf16_rne(x.astype(np.float32))
+    if case == "subnormal":
+        h[M - 1, 7] = 0x0001
+    codes = rng.integers(0, 256, (V, H // 2), dtype=np.uint8)
+    scales = rng.choice(np.r_[0x30:0x4A], (V, H // 16)).astype(np.uint8)
+    g, alpha = 0.01, 0.5
+    got = host_bits(L.logits_nvfp4(bf16_dev(h), u8_dev(codes), u8_dev(scales), g, alpha))
+    ref, A = oracle.lmhead_logits_nvfp4(h, codes, scales, g, alpha, None)
+    check_bf16(got, ref, A, g * alpha, oracle.ulp_bf16, what=f"nvfp4 {case}")
+    wbits = f32_bits_to_bf16_bits_exact(oracle.nvfp4_weight_f64(codes, scales, H).astype(np.float32))
+    s = float(np.float32(g) * np.float32(alpha))
+    for p in PATHS:
+        twin = L.logits(bf16_dev(h), bf16_dev(wbits), s, None, torch.bfloat16, path=p)
+        assert np.array_equal(got, host_bits(twin)), (case, p)
+
+
 def test_hip_graph_capture_and_replay():
     # The entry points allocate, free and synchronise nothing, so they can be
     # captured in a HIP graph (the decode loop of a server). Every replay,
