@@ -387,9 +387,17 @@ __global__ __launch_bounds__(64 * NW, 1) void nvfp4_ring_kernel(
     // chunk's hidden loads, the next scale group
     wait_lds();
     issue_unit(w + NSL, std::integral_constant<int, SLOT>{}, (Q + NSL) % NB);
-    if constexpr ((Q + NSL) % NB == 0)
+    // the batch in this order (direct loads, hidden, scales), as the wait
+    // counts assume: a load issued above a direct load would make the count
+    // that retires that direct load one too large
+    if constexpr ((Q + NSL) % NB == 0) {
+      sched_fence();
       load_hidden(hring[((Q + NSL) / NB) % NHR], (w + NSL) / NB);
-    if constexpr (C8 == GROUP - 1) load_scales(J, w / NB / GROUP + 1);
+    }
+    if constexpr (C8 == GROUP - 1) {
+      sched_fence();
+      load_scales(J, w / NB / GROUP + 1);
+    }
     transpose4(rg.x[0], rg.x[1], rg.x[2], rg.x[3]);
     transpose4(rg.x[4], rg.x[5], rg.x[6], rg.x[7]);
   };
@@ -436,8 +444,15 @@ __global__ __launch_bounds__(64 * NW, 1) void nvfp4_ring_kernel(
     constexpr int W_ = decltype(wc)::value;
     constexpr int VB = W_ - NSL;  // the batch this is
     issue_unit(W_, wc, W_ % NB);
-    if constexpr (W_ % NB == 0) load_hidden(hring[(W_ / NB) % NHR], W_ / NB);
-    if constexpr (S::scl(VB) != 0) load_scales(S::md(VB, NB), 0);
+    if constexpr (W_ % NB == 0) {
+      sched_fence();
+      load_hidden(hring[(W_ / NB) % NHR], W_ / NB);
+    }
+    if constexpr (S::scl(VB) != 0) {
+      sched_fence();
+      load_scales(S::md(VB, NB), 0);
+    }
+    sched_fence();
   });
   wait_vm<S::wait_hidden(-1)>();
   store_hidden(hring[0], 0);

@@ -240,8 +240,13 @@ __global__ __launch_bounds__(64 * NW, NW >= 8 ? 1 : 2) void skinny_kernel(
     // returned (lgkmcnt(0)) before overwriting the slot.
     wait_lds();
     issue_unit(u + NSL, wl, (P + NSL) % NB);
-    if constexpr ((P + NSL) % NB == 0)
+    if constexpr ((P + NSL) % NB == 0) {
+      // the hidden loads after the unit's direct loads, as the wait counts
+      // assume: issued before them, they would make the count that retires
+      // the second direct load one too large
+      sched_fence();
       load_hidden(hring[((P + NSL) / NB) % NHR], (u + NSL) / NB);
+    }
     if constexpr (J == NB - 1) {
       // end of chunk c: hidden chunk c + 1 to LDS, then the barrier that
       // hands both hidden buffers over
@@ -256,7 +261,11 @@ __global__ __launch_bounds__(64 * NW, NW >= 8 ? 1 : 2) void skinny_kernel(
   static_for<NSL>([&](auto wc) {
     constexpr int W_ = decltype(wc)::value;
     issue_unit(W_, wbuf(wc), W_ % NB);
-    if constexpr (W_ % NB == 0) load_hidden(hring[(W_ / NB) % NHR], W_ / NB);
+    if constexpr (W_ % NB == 0) {
+      sched_fence();
+      load_hidden(hring[(W_ / NB) % NHR], W_ / NB);
+    }
+    sched_fence();
   });
   wait_vm<S::wait_hidden(-1)>();
   store_hidden(hring[0], 0);

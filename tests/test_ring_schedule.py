@@ -14,7 +14,11 @@ direct-to-LDS loads with compile-time vmcnt counts from `Schedule` and
   instantiate is checked over several periods, prologue included;
 - in the generated code no direct-to-LDS load is issued while an LDS
   instruction of the same wave is outstanding (a direct load writes LDS on
-  its own path, not behind the wave's earlier reads of the slot it refills).
+  its own path, not behind the wave's earlier reads of the slot it refills);
+- the generated steady-state loop issues its loads in the order the counts
+  assume, each wait at most its count (a hidden or scale load scheduled
+  above a unit's direct load would make the count that retires that direct
+  load one too large; the kernels fence their batches against it).
 """
 import shutil
 import subprocess
@@ -256,3 +260,165 @@ def test_checker_follows_loops():
         s_cbranch_scc1 .LBB0_1
         s_endpgm
     """) == [0]
+
+
+# The generated code issues the loads in the order the wait counts assume.
+# The counts above are right for the source's issue order; the compiler must
+# not move a load across one of the fenced waits. Along the steady-state loop
+# of every instantiation, the sequence of vector memory loads and vmcnt waits
+# must be one schedule period (or several) of the source, rotated to where
+# the loop starts: per unit, a wait of at most the read's count; the unit's
+# two direct loads, the hidden loads of a chunk's first unit, in the NVFP4
+# kernel the two scale loads at a group's last chunk; at a chunk's last unit
+# a wait of at most the hidden count. Extra waits, or waits of smaller
+# counts, only wait longer and are accepted.
+
+_VMCNT_RE = __import__("re").compile(r"vmcnt\((\d+)\)")
+_BRANCH_RE = __import__("re").compile(r"^s_(?:cbranch_\w+|branch)\s+(\.LBB\S+)")
+_SKINNY_RE = __import__("re").compile(r"skinny_kernelILi(\d+)ELi(\d+)ELb\dE\w+?Li(\d+)ELi(\d+)EE")
+_NVRING_RE = __import__("re").compile(r"nvfp4_ring_kernelILi(\d+)ELi(\d+)ELi(\d+)ELi(\d+)EE")
+
+
+def _tokens(lines):
+    out = []
+    for t in lines:
+        op = t.split()[0]
+        if op.startswith("buffer_load"):
+            out.append("D" if t.endswith(" lds") else "L")
+        elif op.startswith(("global_load", "buffer_store", "global_store", "buffer_atomic")):
+            out.append("X")  # no other vector memory operation belongs in the loop
+        elif op == "s_waitcnt":
+            m = _VMCNT_RE.search(t)
+            if m:
+                out.append(int(m.group(1)))
+    return out
+
+
+_HEADER_RE = __import__("re").compile(r"^(\.LBB\S+):\s*;\s*=>This Inner Loop Header", __import__("re").M)
+
+
+def _main_loop(lines, labels, headers):
+    """The loop (a header the compiler marks, to the last branch back to it)
+    whose body holds the most direct loads: (start, end). Code laid out
+    after a loop may branch back into it, so a backward branch alone does
+    not make a loop."""
+    best = None
+    for i, t in enumerate(lines):
+        m = _BRANCH_RE.match(t)
+        if not m or m.group(1) not in headers or m.group(1) not in labels:
+            continue
+        j = labels[m.group(1)]
+        if j <= i:
+            n = sum(1 for k in range(j, i + 1) if lines[k].startswith("buffer_load") and lines[k].endswith(" lds"))
+            if best is None or n > best[0] or (n == best[0] and i > best[2]):
+                best = (n, j, i)
+    assert best is not None and best[0] > 0
+    return best[1], best[2]
+
+
+def _model(kind, NB, NSL, HL, period, table):
+    """One period of the source's loads and waits, unit by unit."""
+    units = []
+    for p in range(period):
+        seq = [("W", table[p][0]), "D", "D"]
+        if (p + NSL) % NB == 0:
+            seq += ["L"] * HL
+        if kind == "nvfp4" and (p // NB) % 8 == 7:
+            seq += ["L", "L"]
+        if p % NB == NB - 1:
+            seq.append(("W", table[p][1]))
+        units.append(seq)
+    return units
+
+
+def _gaps(seq, wait_of):
+    """Loads in order and, per gap before each load, the vmcnt counts in it;
+    the loop body is a cycle, so the gap after the last load joins the first."""
+    loads, gaps, cur = [], [], []
+    for t in seq:
+        w = wait_of(t)
+        if w is None:
+            loads.append(t)
+            gaps.append(cur)
+            cur = []
+        else:
+            cur.append(w)
+    if gaps:
+        gaps[0] = cur + gaps[0]
+    return loads, gaps
+
+
+def _matches(asm, model):
+    """asm (loads and vmcnt counts) against the model (loads and ("W", max)):
+    the same loads in the same order, and in each gap between two loads the
+    smallest asm count at most the smallest count the model needs there
+    (waits between the same two loads act as their minimum)."""
+    al, ag = _gaps(asm, lambda t: t if isinstance(t, int) else None)
+    ml, mg = _gaps(model, lambda t: t[1] if isinstance(t, tuple) else None)
+    if al != ml:
+        return False
+    return all(not m or (a and min(a) <= min(m)) for a, m in zip(ag, mg))
+
+
+def _loop_follows_schedule(kind, NB, NSL, HL, period, table, lines, labels, headers):
+    j, i = _main_loop(lines, labels, headers)
+    asm = _tokens(lines[j:i + 1])
+    if "X" in asm:
+        return False
+    units = _model(kind, NB, NSL, HL, period, table)
+    n_dma = asm.count("D")
+    if n_dma % (2 * period):
+        return False
+    reps = n_dma // (2 * period)
+    for rot in range(period):
+        flat = [t for u in (units[rot:] + units[:rot]) * reps for t in u]
+        if _matches(asm, flat):
+            return True
+    return False
+
+
+def test_generated_loop_issues_loads_in_schedule_order(ring_asm, schedules):
+    kernels = kernel_bodies(ring_asm)
+    checked, bad = 0, []
+    for name, (lines, labels) in kernels.items():
+        # label numbers restart in each compiled file: headers per kernel
+        start = ring_asm.index("\n" + name + ":")
+        headers = set(_HEADER_RE.findall(ring_asm[start:ring_asm.index(".Lfunc_end", start)]))
+        m = _SKINNY_RE.search(name)
+        if m:
+            R, NB, NW, NSL = (int(x) for x in m.groups())
+            kind, HL = "bf16", -(-16 * R * 8 // (64 * NW))
+        else:
+            m = _NVRING_RE.search(name)
+            if not m:
+                continue
+            R, NB, NW, NSL = (int(x) for x in m.groups())
+            kind, HL = "nvfp4", -(-16 * R * 32 // (64 * NW))
+        assert (kind, NB, NSL, HL) in schedules, (name, "instantiation missing from the lists above")
+        period, table = schedules[(kind, NB, NSL, HL)]
+        if not _loop_follows_schedule(kind, NB, NSL, HL, period, table, lines, labels, headers):
+            j, i = _main_loop(lines, labels, headers)
+            bad.append(f"{name} (NB {NB}, NSL {NSL}, HL {HL}): {_tokens(lines[j:i + 1])[:80]}")
+        checked += 1
+    assert not bad, "\n".join(bad)
+    assert checked >= 60
+
+
+def test_schedule_order_check_flags_a_moved_load():
+    # one unit of the bf16 kernel (NB = 1, NSL = 4, HL = 1): wait 5, two
+    # direct loads, one hidden load, wait for the hidden chunk
+    # (the loop is a cycle: the trailing hidden wait shares a gap with the
+    # next unit's leading wait)
+    model = [("W", 5), "D", "D", "L", ("W", 3)] * 2
+    assert _matches([5, "D", "D", "L", 3, 5, "D", "D", "L", 3], model)
+    assert _matches([4, 2, "D", "D", "L", 3, 3, "D", "D", "L", 2], model)  # extra, smaller waits
+    # a load moved above the wait (where no other wait covers it)
+    lead = [("W", 5), "D", "D", "L"] * 2
+    assert _matches([5, "D", "D", "L", 5, "D", "D", "L"], lead)
+    assert not _matches(["D", 5, "D", "L", 5, "D", "D", "L"], lead)
+    # ... and covered by the previous iteration's trailing wait: accepted
+    assert _matches(["D", 5, "D", "L", 3, "D", "D", "L", 3], model)
+    assert not _matches([6, "D", "D", "L", 6, "D", "D", "L", 6], model)    # waits too weak
+    assert not _matches([3, "D", "L", "D", 3, "D", "D", "L", 3], model)    # loads out of order
+    assert not _matches([3, "D", "D", "L", 3, "D", "D", "L", "L"], model)  # a load too many
+    assert not _matches([3, "D", "D", 3, "L", "D", "D", "L", 3], model)    # the hidden load late
