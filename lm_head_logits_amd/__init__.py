@@ -10,6 +10,7 @@ LMHEAD_NOT_HANDLED the caller gets ``NotHandled`` and decides what to do.
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 
 import torch
@@ -58,9 +59,27 @@ def _check(status: int, where: str):
     raise LmHeadError(status, where)
 
 
+# torch's current raw HIP stream of a device index, without building a Stream
+# object per call (the public route below when this build lacks it)
+_raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+
+
 def _stream_handle(device, stream):
-    s = stream if stream is not None else torch.cuda.current_stream(device)
-    return s.cuda_stream
+    if stream is not None:
+        return stream.cuda_stream
+    if _raw_stream is not None:
+        return _raw_stream(device.index if device.index is not None else torch.cuda.current_device())
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+_NO_SWITCH = contextlib.nullcontext()
+
+
+def _device_ctx(device):
+    """The library launches on the current device: make it `device`, switching
+    (and switching back) only when it is another one."""
+    idx = device.index if device.index is not None else torch.cuda.current_device()
+    return _NO_SWITCH if torch.cuda.current_device() == idx else torch.cuda.device(idx)
 
 
 def _need(cond: bool, msg: str):
@@ -104,7 +123,7 @@ def logits(hidden: torch.Tensor, weight: torch.Tensor, alpha: float = 1.0, bias=
         _need(out.is_cuda and out.dtype == out_dtype and out.shape == (M, V) and out.is_contiguous(),
               "out must be a contiguous [M, V] device tensor of out_dtype")
     _same_device(hidden, weight, bias, out)
-    with torch.cuda.device(hidden.device):  # the library launches on the current device
+    with _device_ctx(hidden.device):
         st = _lib.load().lmhead_logits_ex(
             hidden.data_ptr(), M, H, weight.data_ptr(), V, float(alpha),
             bias.data_ptr() if bias is not None else None, in_code, _DTYPES[out_dtype],
@@ -153,7 +172,7 @@ def logits_rowreduce(hidden: torch.Tensor, weight: torch.Tensor, alpha: float = 
     row_argmax = torch.empty(M, dtype=torch.int32, device=dev)
     row_sumexp = torch.empty(M, dtype=torch.float32, device=dev)
     _same_device(hidden, weight, bias, out, workspace)
-    with torch.cuda.device(dev):
+    with _device_ctx(dev):
         st = _lib.load().lmhead_logits_rowreduce(
             hidden.data_ptr(), M, H, weight.data_ptr(), V, float(alpha),
             bias.data_ptr() if bias is not None else None, in_code, _DTYPES[out_dtype],
@@ -199,7 +218,7 @@ def logits_rowreduce_noalloc(hidden: torch.Tensor, weight: torch.Tensor, alpha: 
               f"row outputs must be contiguous [M] device tensors of {dt}")
         outs.append(t)
     _same_device(hidden, weight, bias, out, *outs)
-    with torch.cuda.device(dev):
+    with _device_ctx(dev):
         st = _lib.load().lmhead_logits_rowreduce_noalloc(
             hidden.data_ptr(), M, H, weight.data_ptr(), V, float(alpha),
             bias.data_ptr() if bias is not None else None, in_code, _DTYPES[out_dtype],
@@ -225,7 +244,7 @@ def quantize_nvfp4(weight: torch.Tensor, *, workspace: torch.Tensor | None = Non
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     _need(workspace.is_cuda and workspace.is_contiguous(), "workspace must be a contiguous device tensor")
     _same_device(weight, workspace)
-    with torch.cuda.device(dev):
+    with _device_ctx(dev):
         st = _lib.load().lmhead_quantize_nvfp4(
             weight.data_ptr(), V, H, codes.data_ptr(), scales.data_ptr(), g.data_ptr(),
             workspace.data_ptr(), workspace.numel() * workspace.element_size(),
@@ -258,7 +277,7 @@ def logits_nvfp4(hidden: torch.Tensor, codes: torch.Tensor, scales: torch.Tensor
         _need(out.is_cuda and out.dtype == torch.bfloat16 and out.shape == (M, V)
               and out.is_contiguous(), "out must be a contiguous bf16 [M, V] device tensor")
     _same_device(hidden, codes, scales, bias, out)
-    with torch.cuda.device(hidden.device):  # the library launches on the current device
+    with _device_ctx(hidden.device):
         st = _lib.load().lmhead_logits_nvfp4(
             hidden.data_ptr(), M, H, codes.data_ptr(), scales.data_ptr(), float(global_scale), V,
             float(alpha), bias.data_ptr() if bias is not None else None, out.data_ptr(),
