@@ -92,17 +92,31 @@ def committed_traffic(kernel: str):
 # GPU timing
 # ----------------------------------------------------------------------------
 
+# Untimed load before each timed region. After any idle spell (input
+# generation between workloads, host copies) the GPU's clocks ramp up over
+# roughly the first 20 ms of load: a 43 us NVFP4 call took about 49 us
+# through its first 220 calls, again after 2 s idle, and again on freshly
+# allocated buffers.
+WARM_MS = 50.0
+
+
 def timed_calls(torch, fns, warmup, steps, batches=5):
     """Run `fns` (one step = each fn once) warmup + steps times. Each fn's
     `steps` calls run back to back in `batches` batches, one pair of events
     around each batch and none between calls, so a batch's time is that of
     its kernels (an event recorded between two kernels holds the second back
-    by several microseconds). Returns the step time (ms: events around all
-    steps, divided by steps), the wall time per step (ms) and, per fn, the
-    batches' average launch times (ms)."""
-    for _ in range(warmup):
+    by several microseconds). The untimed warm-up runs `warmup` steps, and
+    more until at least WARM_MS of continuous work has run. Returns the step
+    time (ms: events around all steps, divided by steps), the wall time per
+    step (ms) and, per fn, the batches' average launch times (ms)."""
+    t0 = time.perf_counter()
+    n = 0
+    while n < warmup or (time.perf_counter() - t0) * 1e3 < WARM_MS:
         for f in fns:
             f()
+        n += 1
+        if n % 4 == 0:
+            torch.cuda.synchronize()  # so that the wall clock follows the GPU
     torch.cuda.synchronize()
     nb = max(1, min(batches, steps))
     sizes = [steps // nb + (1 if b < steps % nb else 0) for b in range(nb)]
@@ -549,6 +563,7 @@ def cpu_per_config(wl):
 
 
 def main():
+    global WARM_MS
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
@@ -559,7 +574,10 @@ def main():
                     help="run one workload only (for profiling; 'copy' is the HBM counter "
                          "calibration); the headline line needs decode")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--warm-ms", type=float, default=WARM_MS,
+                    help="untimed work before each timed region, at least (ms)")
     args = ap.parse_args()
+    WARM_MS = max(0.0, args.warm_ms)
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this library shards by vocabulary with no exchange, "
               "and multi-GPU runs are not part of this build. Use --gpus 1.", file=sys.stderr)
@@ -633,7 +651,7 @@ def main():
         "unit": "GB/s",
         "n_gpus": 1,
         "steps": args.steps,
-        "warmup": args.warmup,
+        "warmup": args.warmup, "warmup_min_ms": WARM_MS,
         "ms_per_step": round(step_ms, 4),
         "higher_is_better": True,
         "scaling": "weak",
