@@ -89,7 +89,8 @@ def _need(cond: bool, msg: str):
 
 def _same_device(*tensors):
     devs = {t.device for t in tensors if t is not None}
-    _need(len(devs) == 1, f"all tensors must be on one device, got {sorted(map(str, devs))}")
+    if len(devs) != 1:  # the message only on failure: this runs on every call
+        raise ValueError(f"all tensors must be on one device, got {sorted(map(str, devs))}")
 
 
 _PATHS = {"auto": PATH_AUTO, "skinny": PATH_SKINNY, "tiled": PATH_TILED}
@@ -112,7 +113,8 @@ def logits(hidden: torch.Tensor, weight: torch.Tensor, alpha: float = 1.0, bias=
     _need(hidden.is_contiguous() and weight.is_contiguous(), "inputs must be contiguous")
     M, H = hidden.shape
     V, H2 = weight.shape
-    _need(H == H2, f"hidden has H={H}, weight has H={H2}")
+    if H != H2:
+        raise ValueError(f"hidden has H={H}, weight has H={H2}")
     in_code = _DTYPES[hidden.dtype] if hidden.dtype == weight.dtype else LMHEAD_F32
     if bias is not None:
         _need(bias.is_cuda and bias.dtype == torch.float32 and bias.shape == (V,)
@@ -153,7 +155,8 @@ def logits_rowreduce(hidden: torch.Tensor, weight: torch.Tensor, alpha: float = 
     _need(hidden.is_contiguous() and weight.is_contiguous(), "inputs must be contiguous")
     M, H = hidden.shape
     V, H2 = weight.shape
-    _need(H == H2, f"hidden has H={H}, weight has H={H2}")
+    if H != H2:
+        raise ValueError(f"hidden has H={H}, weight has H={H2}")
     in_code = _DTYPES[hidden.dtype] if hidden.dtype == weight.dtype else LMHEAD_F32
     dev = hidden.device
     if bias is not None:
@@ -201,7 +204,8 @@ def logits_rowreduce_noalloc(hidden: torch.Tensor, weight: torch.Tensor, alpha: 
     _need(hidden.is_contiguous() and weight.is_contiguous(), "inputs must be contiguous")
     M, H = hidden.shape
     V, H2 = weight.shape
-    _need(H == H2, f"hidden has H={H}, weight has H={H2}")
+    if H != H2:
+        raise ValueError(f"hidden has H={H}, weight has H={H2}")
     in_code = _DTYPES[hidden.dtype] if hidden.dtype == weight.dtype else LMHEAD_F32
     dev = hidden.device
     if bias is not None:
@@ -214,8 +218,8 @@ def logits_rowreduce_noalloc(hidden: torch.Tensor, weight: torch.Tensor, alpha: 
     for t, dt in ((row_max, torch.float32), (row_argmax, torch.int32), (row_sumexp, torch.float32)):
         if t is None:
             t = torch.empty(M, dtype=dt, device=dev)
-        _need(t.is_cuda and t.dtype == dt and t.shape == (M,) and t.is_contiguous(),
-              f"row outputs must be contiguous [M] device tensors of {dt}")
+        if not (t.is_cuda and t.dtype == dt and t.shape == (M,) and t.is_contiguous()):
+            raise ValueError(f"row outputs must be contiguous [M] device tensors of {dt}")
         outs.append(t)
     _same_device(hidden, weight, bias, out, *outs)
     with _device_ctx(dev):
@@ -266,8 +270,9 @@ def logits_nvfp4(hidden: torch.Tensor, codes: torch.Tensor, scales: torch.Tensor
           "inputs must be contiguous")
     M, H = hidden.shape
     V = codes.shape[0]
-    _need(codes.shape == (V, H // 2) and H % 2 == 0, f"codes must be [V, H/2] = [{V}, {H // 2}]")
-    _need(H % 16 == 0 and scales.shape == (V, H // 16), f"scales must be [V, H/16]")
+    if not (codes.shape == (V, H // 2) and H % 2 == 0):
+        raise ValueError(f"codes must be [V, H/2] = [{V}, {H // 2}]")
+    _need(H % 16 == 0 and scales.shape == (V, H // 16), "scales must be [V, H/16]")
     if bias is not None:
         _need(bias.is_cuda and bias.dtype == torch.float32 and bias.shape == (V,)
               and bias.is_contiguous(), "bias must be a contiguous fp32 device tensor [V]")
